@@ -1,0 +1,135 @@
+"""Seeded synthetic inputs for exact tiled attention.
+
+This module is the only code shared by the HIP path's callers (tests, bench,
+smoke) and the CPU oracle. It draws random numbers and rounds them to BF16; it
+holds none of the attention arithmetic.
+
+Workloads follow the shapes the three source pages use:
+  * "FlashAttention HBM bytes, one head, 8K" (one head, N=8192, d=128, BF16,
+    with causal and GQA-decode follow-ups),
+  * "Flash Attention Mechanics" (32 heads, d=128; a seq-1024, d-64 harness),
+  * "Why is standard attention memory-bound" (one head, N=4096/8192).
+Values are i.i.d. N(0,1) drawn in float32 with numpy's PCG64 generator
+(``np.random.default_rng(seed)``), in the order Q, K, V, then rounded to the
+nearest BF16 (ties to even).
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- BF16 bits
+
+def bf16_round_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to BF16 (nearest, ties to even); return uint16 bits.
+
+    NaN stays a quiet NaN; infinities and overflow to infinity follow IEEE RNE.
+    """
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    out = rounded.astype(np.uint16)
+    nan = np.isnan(x)
+    if nan.any():
+        out[nan] = ((u[nan] >> 16) | 0x40).astype(np.uint16)
+    return out
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen BF16 bits to float32 exactly (the BF16 value is a float32 prefix)."""
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32)
+
+
+def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    """One N(0,1) float32 draw of ``shape`` rounded to BF16 bits."""
+    return bf16_round_bits(rng.standard_normal(size=shape, dtype=np.float32))
+
+
+# ---------------------------------------------------------------- workloads
+
+@dataclasses.dataclass(frozen=True)
+class FwdCase:
+    """A forward workload: Q,O [B,Hq,N,d]; K,V [B,Hkv,N,d]; all BF16."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    N: int
+    d: int
+    causal: bool
+    seed: int
+    sampled_rows: int | None = None  # rows per head the oracle checks (None = all)
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+@dataclasses.dataclass(frozen=True)
+class DecodeCase:
+    """A decode workload: Q,O [B,Hq,1,d]; K,V [B,Hkv,L,d]; split-KV."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    L: int
+    d: int
+    num_splits: int
+    seed: int
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+
+# The five workloads. Seeds 1..5 in order.
+TINY = FwdCase("1x1x128 d64", 1, 1, 1, 128, 64, False, seed=1)
+ONE_HEAD_8K = FwdCase("1x1x8192 d128", 1, 1, 1, 8192, 128, False, seed=2)
+ONE_HEAD_8K_CAUSAL = dataclasses.replace(ONE_HEAD_8K, name="1x1x8192 d128 causal", causal=True)
+HEADS32_4K = FwdCase("1x32x4096 d128", 1, 32, 32, 4096, 128, False, seed=3, sampled_rows=1024)
+HEADS32_4K_CAUSAL = dataclasses.replace(HEADS32_4K, name="1x32x4096 d128 causal", causal=True)
+LONG_128K = FwdCase("1x8x131072 d128 causal", 1, 8, 8, 131072, 128, True, seed=4, sampled_rows=1024)
+DECODE_GQA = DecodeCase("decode B16 Hq32 Hkv8 L8192 d128 s16", 16, 32, 8, 8192, 128, 16, seed=5)
+
+
+def fwd_inputs(case: FwdCase):
+    """(q, k, v) BF16 bit arrays for a forward workload, drawn Q, K, V in order."""
+    rng = np.random.default_rng(case.seed)
+    q = normal_bf16(rng, (case.B, case.Hq, case.N, case.d))
+    k = normal_bf16(rng, (case.B, case.Hkv, case.N, case.d))
+    v = normal_bf16(rng, (case.B, case.Hkv, case.N, case.d))
+    return q, k, v
+
+
+def decode_inputs(case: DecodeCase):
+    """(q, k, v) BF16 bit arrays for a decode workload: q [B,Hq,1,d]."""
+    rng = np.random.default_rng(case.seed)
+    q = normal_bf16(rng, (case.B, case.Hq, 1, case.d))
+    k = normal_bf16(rng, (case.B, case.Hkv, case.L, case.d))
+    v = normal_bf16(rng, (case.B, case.Hkv, case.L, case.d))
+    return q, k, v
+
+
+def sample_rows(seed: int, head: int, N: int, count: int, boundary: int = 64) -> np.ndarray:
+    """Sorted seeded sample of ``count`` query rows for one head.
+
+    Rows 0 and N-1 and the rows on each side of a few ``boundary``-multiples
+    are always included; the rest are drawn without replacement from
+    ``default_rng(seed*1000 + head)``.
+    """
+    if count >= N:
+        return np.arange(N, dtype=np.int64)
+    forced = {0, N - 1}
+    for t in (1, 2, N // (2 * boundary), N // boundary - 1):
+        c = t * boundary
+        if 0 < c < N:
+            forced.update((c - 1, c))
+    forced = sorted(r for r in forced if 0 <= r < N)[:count]
+    rng = np.random.default_rng(seed * 1000 + head)
+    pool = np.setdiff1d(np.arange(N, dtype=np.int64), np.array(forced, dtype=np.int64))
+    extra = rng.choice(pool, size=count - len(forced), replace=False)
+    return np.sort(np.concatenate([np.array(forced, dtype=np.int64), extra]))
