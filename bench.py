@@ -1,0 +1,248 @@
+#!/usr/bin/env python3
+"""Benchmark of exact tiled attention on one MI355X; prints ONE JSON line.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  * forward, one head, N = 8192, d = 128, BF16, non-causal (the headline case),
+  * forward on the same inputs, causal,
+  * split-KV GQA decode: B = 16, Hq = 32, Hkv = 8, L = 8192, d = 128, 16 chunks.
+Inputs are seeded N(0,1) draws rounded to BF16 and resident in HBM before the
+timed region. `value` is the non-causal forward's algorithmic TFLOP/s
+(4 N^2 d per launch over the launch's average duration, measured with HIP
+events on the stream the kernel runs on). The decode rate is reported as
+algorithmic HBM GB/s (K and V read once per KV head).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --calibrate-copy   (plain copy kernel of known size, for
+                                           normalising hardware byte counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s & % BF16 MFMA peak (N=8K,d=128); decode HBM GB/s"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_1x1x8192_d128_counters.txt")
+KERNEL_SOURCES = ["fa_fwd.hip", "fa_device.h", "fa_launch.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "exact_tiled_attention_fa_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per forward launch from the committed counter summary, if current."""
+    if not os.path.exists(COUNTERS_FILE):
+        return None
+    fields = {}
+    for line in open(COUNTERS_FILE):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    if fields.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def calibrate_copy() -> None:
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
+
+
+def cpu_baseline(case, seconds: float) -> dict:
+    """The FP64 oracle as it stands, timed on this host's cores over whole passes of the workload."""
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import fa_oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:  # threadpoolctl missing: report the affinity set
+        cores = len(os.sched_getaffinity(0))
+    qb, kb, vb = si.fwd_inputs(case)
+    q, k, v = (si.bf16_bits_to_f32(x) for x in (qb, kb, vb))
+    rows_total = 0
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        fa_oracle.attention_ref(q, k, v, case.causal, case.scale)
+        passes += 1
+        rows_total += case.N
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    flops = passes * 4.0 * case.N * case.N * case.d
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{passes} full pass(es) of the 1x1x8192 d128 non-causal forward ({rows_total} rows) "
+                      f"in {dt:.1f} s, FP64 NumPy three-pass attention"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="bounded CPU oracle sample length")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary (non-step) measurements")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the forward shards by head "
+              "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr, flush=True)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_fa_amd as fa
+    import seeded_inputs as si
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    if args.calibrate_copy:
+        calibrate_copy()
+        return 0
+
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    fcase = si.ONE_HEAD_8K
+    q, k, v = (up(x) for x in si.fwd_inputs(fcase))
+    o = torch.empty_like(q)
+    lse = torch.empty((1, 1, fcase.N), dtype=torch.float32, device=dev)
+    o_c = torch.empty_like(q)
+    lse_c = torch.empty_like(lse)
+    dcase = si.DECODE_GQA
+    dq, dk, dv = (up(x) for x in si.decode_inputs(dcase))
+    do = torch.empty_like(dq)
+    dlse = torch.empty((dcase.B, dcase.Hq), dtype=torch.float32, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(dcase.B, dcase.Hq, dcase.L, dcase.d, dcase.num_splits),
+                     dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = {name: [] for name in ("fwd", "fwd_causal", "decode")}
+
+    def step(record: bool):
+        def timed(name, fn):
+            if record:
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                ev[name].append((a, b))
+            else:
+                fn()
+        timed("fwd", lambda: fa.fwd(q, k, v, causal=False, scale=fcase.scale, out=o, lse=lse))
+        timed("fwd_causal", lambda: fa.fwd(q, k, v, causal=True, scale=fcase.scale, out=o_c, lse=lse_c))
+        timed("decode", lambda: fa.decode(dq, dk, dv, num_splits=dcase.num_splits, scale=dcase.scale,
+                                          workspace=ws, out=do, lse=dlse))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
+
+    def mean_s(name):
+        xs = [a.elapsed_time(b) for a, b in ev[name]]
+        return sum(xs) / len(xs) * 1e-3
+
+    t_fwd, t_fwd_c, t_dec = mean_s("fwd"), mean_s("fwd_causal"), mean_s("decode")
+    flops = 4.0 * fcase.N * fcase.N * fcase.d
+    tflops = flops / t_fwd / 1e12
+    tflops_c = flops / 2 / t_fwd_c / 1e12
+    kv_bytes = 2 * dcase.B * dcase.Hkv * dcase.L * dcase.d * 2
+    dec_gbs = kv_bytes / t_dec / 1e9
+
+    extra = {}
+    if not args.no_extra:
+        for case in (si.HEADS32_4K, si.HEADS32_4K_CAUSAL):
+            q3, k3, v3 = (up(x) for x in si.fwd_inputs(case))
+            o3 = torch.empty_like(q3)
+            l3 = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
+            for _ in range(3):
+                fa.fwd(q3, k3, v3, causal=case.causal, out=o3, lse=l3)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 10
+            a.record(stream)
+            for _ in range(reps):
+                fa.fwd(q3, k3, v3, causal=case.causal, out=o3, lse=l3)
+            b.record(stream)
+            torch.cuda.synchronize()
+            t = a.elapsed_time(b) * 1e-3 / reps
+            fl = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
+            key = "fwd_1x32x4096_d128" + ("_causal" if case.causal else "")
+            extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                          "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del q3, k3, v3, o3, l3
+
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "fwd 1 head N=8192 d=128 non-causal (step also runs the causal fwd and a "
+                               "B16 Hq32 Hkv8 L8192 16-split decode)",
+                   "batch": 1, "heads": 1, "seq_len": 8192, "head_dim": 128, "causal": False},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_BF16_TFLOPS, 5), "traffic": traffic},
+        "fwd_us": round(t_fwd * 1e6, 2),
+        "fwd_causal_tflops": round(tflops_c, 3),
+        "fwd_causal_us": round(t_fwd_c * 1e6, 2),
+        "decode_hbm_gbs": round(dec_gbs, 1),
+        "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
+        "decode_us": round(t_dec * 1e6, 2),
+        "also": extra,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(fcase, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

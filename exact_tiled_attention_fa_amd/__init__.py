@@ -1,0 +1,95 @@
+"""exact_tiled_attention_fa_amd: exact tiled (FlashAttention-style) attention on MI355X.
+
+Thin Python binding over the C ABI in include/fa.h (libfa.so, hand-written HIP
+kernels for gfx950). torch supplies device memory and the current stream
+only; every step of the computation runs in the library's kernels.
+
+    o, lse = fwd(q, k, v, causal=False, scale=None)
+    o, lse = decode(q, k, v, num_splits=16, scale=None)
+"""
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import _lib
+from ._lib import FaError
+
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "FaError"]
+
+
+def _stream_handle(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _check_bf16(name: str, t: torch.Tensor, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if t.dtype != torch.bfloat16:
+        raise TypeError(f"{name} must be bfloat16 (got {t.dtype})")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims (got shape {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+        scale: float | None = None, out: torch.Tensor | None = None,
+        lse: torch.Tensor | None = None):
+    """Attention forward. q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 -> (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError(f"k and v must be [B,Hkv,N,d] = {(B, Hkv, N, d)}; got {tuple(k.shape)}, {tuple(v.shape)}")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _check_bf16("out", out, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    st = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                           B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(q.device))
+    _lib.check(st, "fa_fwd")
+    return out, lse
+
+
+def decode_workspace_bytes(B: int, Hq: int, L: int, d: int, num_splits: int) -> int:
+    return int(_lib.lib().fa_decode_workspace_bytes(B, Hq, L, d, num_splits))
+
+
+def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 16,
+           scale: float | None = None, workspace: torch.Tensor | None = None,
+           out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
+    """Split-KV decode. q [B,Hq,1,d], k/v [B,Hkv,L,d] bf16 -> (o [B,Hq,1,d] bf16, lse [B,Hq] fp32)."""
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(name, t, 4)
+    B, Hq, one, d = q.shape
+    if one != 1:
+        raise ValueError("decode takes one query token per sequence: q must be [B,Hq,1,d]")
+    Hkv, L = k.shape[1], k.shape[2]
+    if k.shape != (B, Hkv, L, d) or v.shape != k.shape:
+        raise ValueError("k and v must be [B,Hkv,L,d]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    need = decode_workspace_bytes(B, Hq, L, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    st = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                              B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
+                              workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+    _lib.check(st, "fa_decode")
+    return out, lse

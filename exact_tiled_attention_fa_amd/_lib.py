@@ -1,0 +1,62 @@
+"""ctypes loader for libfa.so: declares the C ABI of include/fa.h.
+
+There is no fallback: if the library is missing the calls raise, so nothing
+silently runs anywhere but the HIP kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+STATUS_NAMES = {
+    0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEAD_DIM", -4: "FA_ERR_GQA",
+    -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
+}
+
+_lib = None
+
+
+class FaError(RuntimeError):
+    """A libfa call returned a non-zero status."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = _load().fa_status_string(status).decode()
+        super().__init__(f"{where}: {msg} (status {status})")
+
+
+def _declare(lib):
+    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd.restype = i
+    lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
+    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_decode.restype = i
+    lib.fa_status_string.argtypes = [i]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is not built; run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "or `python exact_tiled_attention_fa_amd/build.py`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def lib():
+    return _load()
+
+
+def check(status: int, where: str) -> None:
+    if status != FA_OK:
+        raise FaError(status, where)

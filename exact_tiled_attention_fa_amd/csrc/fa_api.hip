@@ -1,0 +1,131 @@
+// C ABI of libfa: argument checks (host only, before any HIP call), launch
+// configuration and dispatch to the kernel translation units.
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Elements of a [B, H, N, d] tensor, or -1 if it does not fit in int64.
+int64_t elems(int64_t B, int64_t H, int64_t N, int64_t d) {
+  const int64_t lim = INT64_MAX / 4;
+  int64_t x = B;
+  for (int64_t f : {H, N, d}) {
+    if (f != 0 && x > lim / f) return -1;
+    x *= f;
+  }
+  return x;
+}
+
+int decode_chunk(int L, int num_splits) { return (L + num_splits - 1) / num_splits; }
+int decode_splits_used(int L, int num_splits) {
+  const int chunk = decode_chunk(L, num_splits);
+  return (L + chunk - 1) / chunk;
+}
+
+int next_pow2_le16(int g) {
+  int p = 1;
+  while (p < g && p < 16) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+extern "C" const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128";
+    case FA_ERR_GQA: return "FA_ERR_GQA: Hq must be a multiple of Hkv";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
+    case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
+    case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0 or 1 and scale finite";
+    default: return "unknown fa_status";
+  }
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if (causal != 0 && causal != 1) return FA_ERR_ARG;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+  if (elems(B, Hq, N, d) < 0) return FA_ERR_SHAPE;
+  const int64_t nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
+  const int64_t nwg = (int64_t)B * Hq * nqb;
+  if (nwg > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N;
+  a.c = scale * fa::kLog2eHost;
+  a.nqb = (int)nqb;
+  a.nwg = (int)nwg;
+  const hipError_t e = fa::launch_fwd(a, d, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits) {
+  if (B <= 0 || Hq <= 0 || L <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > L) return 0;
+  const int S = decode_splits_used(L, num_splits);
+  const int64_t rows = (int64_t)B * Hq;
+  const int64_t floats = rows * S * (int64_t)d + rows * S;
+  const size_t bytes = (size_t)floats * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
+                         void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
+  if (Hq % Hkv != 0) return FA_ERR_GQA;
+  if (num_splits < 1 || num_splits > L) return FA_ERR_SHAPE;
+  if (!isfinite(scale)) return FA_ERR_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+  if (elems(B, Hkv, L, d) < 0 || elems(B, Hq, 1, d) < 0) return FA_ERR_SHAPE;
+  const size_t need = fa_decode_workspace_bytes(B, Hq, L, d, num_splits);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+
+  const int G = Hq / Hkv;
+  const int gm = G <= 16 ? next_pow2_le16(G) : 16;
+  const int n_hg = (G + gm - 1) / gm;
+  const int S = decode_splits_used(L, num_splits);
+  const int64_t nwg = (int64_t)B * Hkv * n_hg * S;
+  if (nwg > INT32_MAX || (int64_t)B * Hq > INT32_MAX) return FA_ERR_SHAPE;
+
+  fa::DecArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o_part = static_cast<float*>(workspace);
+  a.lse_part = a.o_part + (size_t)B * Hq * S * d;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.L = L;
+  a.chunk = decode_chunk(L, num_splits);
+  a.S = S;
+  a.G = G;
+  a.n_hg = n_hg;
+  a.c = scale * fa::kLog2eHost;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = fa::launch_decode_split(a, d, gm, s);
+  if (e != hipSuccess) return FA_ERR_LAUNCH;
+  e = fa::launch_combine(a.o_part, a.lse_part, static_cast<uint16_t*>(o), lse, B * Hq, S, d, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}

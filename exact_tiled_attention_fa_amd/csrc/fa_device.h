@@ -1,0 +1,98 @@
+// Device-side building blocks for the gfx950 attention kernels: vector types,
+// MFMA wrappers, LDS transpose reads, cross-lane exchanges and BF16 packing.
+//
+// Register layouts (CDNA4 MFMA, wave64; lane l, element/register index e/r):
+//   v_mfma_f32_32x32x16_bf16  D[32x32] = A[32x16] B[16x32] + C
+//     A: lane l holds A[l%32][8*(l/32) + e], e = 0..7
+//     B: lane l holds B[8*(l/32) + e][l%32]
+//     C: lane l reg r holds C[8*(r/4) + 4*(l/32) + r%4][l%32], r = 0..15
+//   v_mfma_f32_16x16x32_bf16  D[16x16] = A[16x32] B[32x16] + C
+//     A: lane l holds A[l%16][8*(l/16) + e]
+//     B: lane l holds B[8*(l/16) + e][l%16]
+//     C: lane l reg r holds C[4*(l/16) + r][l%16], r = 0..3
+// Only the pairing of A's and B's k-slots matters for a contraction, so the
+// kernels are free to choose which k index lives in which slot, as long as A
+// and B agree.
+//
+//   ds_read_b64_tr_b16: within each block of 16 lanes, lane t names an 8-byte
+//   run of 4 b16 values; lane i receives element (i%4) of the runs named by
+//   lanes i/4, 4 + i/4, 8 + i/4, 12 + i/4. With lane t pointing at row t/4,
+//   columns 4*(t%4)..+3 of a row-major b16 matrix, lane i gets column i of
+//   those 4 rows: a transposed 4x16 read.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// log2(x) (v_log_f32).
+__device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of x in the lane 32 away (l ^ 32), combined with the own value.
+__device__ __forceinline__ float max_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// x from lane l ^ mask (any mask < 64), through the LDS crossbar.
+__device__ __forceinline__ float shfl_xor(float x, int mask) {
+  const int lane = __lane_id();
+  return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ mask) << 2, __float_as_int(x)));
+}
+
+// Round-to-nearest-even FP32 -> BF16 of 8 values (v_cvt_pk_bf16_f32 pairs).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3,
+                                              float a4, float a5, float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+// Transposed 4x16 read of b16 values from LDS (see the header comment).
+__device__ __forceinline__ i16x4 lds_read_tr(const void* lds_byte_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(lds_byte_ptr));
+}
+
+__device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
+  i16x8 c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Work-group id -> logical id such that each XCD (work-groups are handed to
+// the 8 XCDs round-robin) receives one contiguous range of logical ids.
+__device__ __forceinline__ int xcd_contiguous(int wg, int nwg) {
+  const int q = nwg >> 3, r = nwg & 7;
+  const int x = wg & 7, k = wg >> 3;
+  return x * q + (x < r ? x : r) + k;
+}
+
+}  // namespace fa

@@ -1,0 +1,277 @@
+// Exact tiled attention forward pass for gfx950.
+//
+// What it computes: O = softmax(scale Q K^T) V and lse = ln sum exp(scale q.k),
+// tiled with the online softmax ("Flash Attention Mechanics: How Tiled
+// Attention Fits in SRAM", section "The Tiling Algorithm"; "Why is standard
+// attention memory-bound, and how does FlashAttention fix it?", "Step 3"). The
+// query-outer loop order follows the FA2 schedule described in "FlashAttention
+// HBM bytes, one head, 8K" ("A strong answer"): each work-group owns one query
+// block, streams every K/V tile of its head, and writes its O tile once.
+//
+// Mapping onto CDNA4:
+//   * 256 threads = 4 waves; each wave owns 32 query rows (128 per work-group).
+//   * K/V tiles of 64 keys are staged in LDS, double buffered: the next tile's
+//     global loads are issued before the current tile's math and written to
+//     the other buffer after it, so one barrier per tile suffices.
+//   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
+//     (A = K from LDS, B = Q^T held in registers for the whole sweep). In the
+//     result each lane holds 16 keys of ONE query row, so the row max and row
+//     sum are in-lane reductions plus one permlane32 swap, and the same
+//     registers, rounded to BF16, are directly the B operand (P^T) of the
+//     second product O^T = V^T P^T -- no LDS round trip for P.
+//   * V^T operands come from LDS with ds_read_b64_tr_b16 (transposed reads).
+//   * Softmax in base 2: t = s * scale * log2(e); p = 2^(t - m); the partial O
+//     is rescaled by 2^(m_old - m_new), skipped when no row's max moved.
+//   * Causal: K/V tiles past the block's last row are never loaded; a wave
+//     skips the math of tiles wholly above its rows; only the diagonal tiles
+//     (and a ragged tail) take the masked path.
+//   * Grid: logical id -> (batch, head, query block) with the query blocks of
+//     a head adjacent (heaviest first when causal), and logical ids laid out so
+//     that each XCD gets one contiguous range: a head's K/V is then shared in
+//     one XCD's L2.
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+template <int D>
+struct FwdCfg {
+  static constexpr int CPR = D / 8;                         // 16-byte chunks per row
+  static constexpr int TILE_CHUNKS = kFwdKeys * CPR;        // chunks in one K or V tile
+  static constexpr int CPT = TILE_CHUNKS / kFwdThreads;     // chunks per thread per tile
+  static constexpr int KK = D / 16;                         // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;                         // 32-wide d tiles of O^T
+};
+
+// LDS placement of 16-byte chunk `c` of tile row `r` (in chunks). The XOR
+// swizzles keep the two read patterns free of bank conflicts: K fragment reads
+// (32 rows, one chunk column) and V transposed reads (4 rows x 4 chunks).
+template <int D>
+__device__ __forceinline__ int k_slot(int r, int c) {
+  return D == 128 ? r * 16 + (c ^ (r & 15)) : r * 8 + (c ^ ((r >> 1) & 7));
+}
+template <int D>
+__device__ __forceinline__ int v_slot(int r, int c) {
+  return D == 128 ? r * 16 + (c ^ ((r & 3) << 2)) : r * 8 + (c ^ (((r >> 1) & 1) << 2));
+}
+
+__device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float a3) {
+  __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1, b2 = (__bf16)a2, b3 = (__bf16)a3;
+  uint2 r;
+  r.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  r.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+  return r;
+}
+
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(kFwdThreads) void fa_fwd_kernel(FwdArgs a) {
+  using C = FwdCfg<D>;
+  __shared__ uint4 lds_k[2][C::TILE_CHUNKS];
+  __shared__ uint4 lds_v[2][C::TILE_CHUNKS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int g = lane >> 5;    // which half of the wave (k-slot group)
+  const int li = lane & 31;   // query row within the wave / column of S^T
+
+  // ---- grid order: XCD-contiguous, head-major, heaviest query block first when causal
+  const int lid = xcd_contiguous(blockIdx.x, a.nwg);
+  const int bh = lid / a.nqb;
+  int qb = lid - bh * a.nqb;
+  if (CAUSAL) qb = a.nqb - 1 - qb;
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int N = a.N;
+  const int q0 = qb * kFwdRows;
+  const size_t qo_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
+  const size_t kv_base = (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+
+  // ---- Q^T operand of this lane's row, kept in registers for the whole sweep.
+  // A negative scale is folded into Q (sign flip is exact), so the kernel
+  // always works with c = |scale| log2(e) >= 0 and max(t) = c max(s).
+  const int qi = q0 + wave * 32 + li;
+  const uint32_t sign = a.c < 0.f ? 0x80008000u : 0u;
+  const float c = fabsf(a.c);
+  bf16x8 qf[C::KK];
+  {
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + qo_base + (size_t)(qi < N ? qi : 0) * D);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      uint4 w = qi < N ? qrow[2 * kk + g] : make_uint4(0u, 0u, 0u, 0u);
+      w.x ^= sign; w.y ^= sign; w.z ^= sign; w.w ^= sign;
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+
+  const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
+  const int n_tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
+  const int wave_q0 = q0 + wave * 32;
+  const int wave_q1 = wave_q0 + 31;
+
+  uint4 kr[C::CPT], vr[C::CPT];
+  auto load_tile = [&](int kv0) {
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x) {
+      const int idx = tid + x * kFwdThreads;
+      const int row = idx / C::CPR, ch = idx % C::CPR;
+      const int key = kv0 + row;
+      if (key < N) {
+        const size_t off = kv_base + (size_t)key * D + ch * 8;
+        kr[x] = *reinterpret_cast<const uint4*>(a.k + off);
+        vr[x] = *reinterpret_cast<const uint4*>(a.v + off);
+      } else {
+        kr[x] = make_uint4(0u, 0u, 0u, 0u);
+        vr[x] = make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int x = 0; x < C::CPT; ++x) {
+      const int idx = tid + x * kFwdThreads;
+      const int row = idx / C::CPR, ch = idx % C::CPR;
+      lds_k[buf][k_slot<D>(row, ch)] = kr[x];
+      lds_v[buf][v_slot<D>(row, ch)] = vr[x];
+    }
+  };
+
+  float m_run = -INFINITY;  // running max of t (base-2 scaled scores) for row qi
+  float l_run = 0.f;        // running sum of 2^(t - m) over this lane's keys
+  f32x16 oacc[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
+
+  // Lane-dependent parts of the V^T transposed-read addresses.
+  const int t16 = lane & 15;
+  const int vch = (lane >> 4) & 1;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int kv0 = t * kFwdKeys;
+    const bool has_next = t + 1 < n_tiles;
+    if (has_next) load_tile(kv0 + kFwdKeys);
+    const int buf = t & 1;
+    if (!CAUSAL || kv0 <= wave_q1) {
+      const char* kb = reinterpret_cast<const char*>(lds_k[buf]);
+      const char* vb = reinterpret_cast<const char*>(lds_v[buf]);
+
+      // ---- S^T = K Q^T for two 32-key sub-tiles.
+      f32x16 s[2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt) {
+        s[jt] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < C::KK; ++kk) {
+          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + 16 * k_slot<D>(jt * 32 + li, 2 * kk + g));
+          s[jt] = mfma32(kf, qf[kk], s[jt]);
+        }
+      }
+
+      // ---- online softmax; lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4 of row qi.
+      const bool need_mask = (kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0);
+      if (need_mask) {
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = kv0 + jt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+            const bool ok = key < N && (!CAUSAL || key <= qi);
+            if (!ok) s[jt][r] = -INFINITY;
+          }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jt][r]);
+      mx = max_xor32(mx);
+      const float mt = mx == -INFINITY ? -INFINITY : mx * c;
+      const float m_new = fmaxf(m_run, mt);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = exp2_hw(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float p = exp2_hw(fmaf(s[jt][r], c, -m_use));
+          if (need_mask) p = s[jt][r] == -INFINITY ? 0.f : p;
+          s[jt][r] = p;
+          rs += p;
+        }
+      l_run = fmaf(l_run, alpha, rs);
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+      }
+
+      // ---- P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
+      //      32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+          pb[jt][hh] = pack_bf16x8(s[jt][8 * hh + 0], s[jt][8 * hh + 1], s[jt][8 * hh + 2], s[jt][8 * hh + 3],
+                                   s[jt][8 * hh + 4], s[jt][8 * hh + 5], s[jt][8 * hh + 6], s[jt][8 * hh + 7]);
+
+      // ---- O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32
+      //      at the same 8 keys, gathered with two transposed reads of 4 keys each.
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) {
+        const int col = 32 * dt + 16 * vch + 4 * (t16 & 3);
+        const int chunk = col >> 3;
+        const int half = (t16 & 1) * 8;
+#pragma unroll
+        for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int row0 = jt * 32 + 16 * hh + 4 * g + (t16 >> 2);
+            const i16x4 lo = lds_read_tr(vb + 16 * v_slot<D>(row0, chunk) + half);
+            const i16x4 hi = lds_read_tr(vb + 16 * v_slot<D>(row0 + 8, chunk) + half);
+            oacc[dt] = mfma32(join_bf16x8(lo, hi), pb[jt][hh], oacc[dt]);
+          }
+      }
+    }
+    if (has_next) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: O = O / l (BF16, round to nearest even), lse = (m + log2 l) ln 2.
+  const float l_tot = sum_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qi < N) {
+    uint16_t* orow = a.o + qo_base + (size_t)qi * D;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        const uint2 w = pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
+                                    oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
+        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * g) = w;
+      }
+    if (g == 0)
+      a.lse[(size_t)(b * a.Hq + h) * N + qi] = l_tot > 0.f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(a.nwg), dim3(kFwdThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
+  return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
+}
+
+}  // namespace fa

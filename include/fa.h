@@ -1,0 +1,113 @@
+/*
+ * fa.h -- C ABI of libfa, exact tiled attention for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (all entry points): exact attention
+ *     O = softmax(scale * Q K^T) V,   lse_i = ln sum_j exp(scale * q_i . k_j),
+ * computed as tiled attention with an online softmax (running row max m,
+ * running sum l, partial O rescaled by exp(m_old - m_new)), never writing the
+ * score matrix S or the weight matrix P to memory.
+ *   - Definition: "Flash Attention Mechanics: How Tiled Attention Fits in SRAM",
+ *     section "Why Standard Attention Is Memory-Bound"; "Why is standard
+ *     attention memory-bound, and how does FlashAttention fix it?", "Step 1".
+ *   - Tiling and the online softmax: the same Mechanics page, section "The
+ *     Tiling Algorithm"; the memory-bound page, "Step 3" and "What is online
+ *     softmax?".
+ *   - Causal tile skipping and decode: "FlashAttention HBM bytes, one head, 8K",
+ *     section "What interviewers probe next".
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. The library never
+ *     frees them and keeps no reference after the call returns.
+ *   - BF16 tensors are IEEE bfloat16 bit patterns; every tensor is contiguous
+ *     (row-major in the order its shape is written) and 16-byte aligned.
+ *   - Argument checks run on the host before any HIP call. On failure the call
+ *     returns a negative fa_status and launches nothing; outputs are untouched.
+ *   - Work is enqueued asynchronously on `stream` (NULL = the null stream). A
+ *     launch failure returns FA_ERR_LAUNCH; faults during execution surface at
+ *     the caller's next synchronisation.
+ *   - GQA: query head h reads KV head h / (Hq / Hkv).
+ *   - scale is used exactly as given (any finite value, including 0 and
+ *     negative); the usual choice is 1/sqrt(d).
+ *   - The functions are thread-safe; concurrent calls on different streams do
+ *     not share memory unless the caller passes the same buffers.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Same object as hipStream_t, declared without the HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t* fa_stream_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,      /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or num_splits out of range */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
+  FA_ERR_GQA = -4,       /* Hq is not a multiple of Hkv */
+  FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
+  FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
+  FA_ERR_LAUNCH = -7,    /* a HIP launch or allocation failed */
+  FA_ERR_ARG = -8        /* causal not 0/1, or scale not finite */
+} fa_status;
+
+/*
+ * fa_fwd -- attention forward pass (prefill), one kernel launch per call.
+ *
+ *   q   [B, Hq,  N, d] bf16   queries
+ *   k   [B, Hkv, N, d] bf16   keys
+ *   v   [B, Hkv, N, d] bf16   values
+ *   o   [B, Hq,  N, d] bf16   output, written once, rounded to nearest even
+ *   lse [B, Hq,  N]    fp32   natural-log logsumexp of each row's scaled scores
+ *   causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
+ *
+ * d must be 64 or 128.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           fa_stream_t stream);
+
+/*
+ * fa_decode_workspace_bytes -- size of the caller-provided workspace that
+ * fa_decode needs for these sizes: FP32 partial outputs [B, Hq, S, d] and
+ * partial logsumexps [B, Hq, S], S = number of non-empty chunks. Returns 0 for
+ * invalid sizes.
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits);
+
+/*
+ * fa_decode -- split-KV decode: one query token per (sequence, query head)
+ * against a KV cache of L keys ("What interviewers probe next", decode; "Does
+ * FlashAttention help when generating one token at a time?").
+ *
+ *   q   [B, Hq,  1, d] bf16
+ *   k   [B, Hkv, L, d] bf16
+ *   v   [B, Hkv, L, d] bf16
+ *   o   [B, Hq,  1, d] bf16
+ *   lse [B, Hq]        fp32 (natural log)
+ *   workspace: device buffer of at least fa_decode_workspace_bytes(...) bytes,
+ *   16-byte aligned, owned by the caller; its contents on entry are ignored.
+ *
+ * The L keys are cut into chunks of ceil(L / num_splits) keys (1 <= num_splits
+ * <= L). One launch computes, per (sequence, KV head, chunk), the chunk's
+ * normalised partial output and logsumexp for every query head of the group,
+ * reading each K/V byte once; a second launch merges the chunks with the
+ * log-sum-exp combine. Two calls that share a workspace must be ordered.
+ */
+int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
+              void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

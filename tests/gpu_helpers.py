@@ -1,0 +1,71 @@
+"""Shared helpers for the GPU parity tests (device upload and the error gates).
+
+Tolerances:
+  * official: O max abs error <= 1e-2; lse error |dlse| / max(|lse|, 1) <= 1e-3
+    (the lse denominator is floored at 1 because causal early rows have lse near 0).
+  * internal, element-wise, derived from the kernel's arithmetic. The kernel
+    computes O_i = sum_j bf16(p_ij) v_j / l_i with p and l in FP32 and rounds O
+    to BF16 once. With bf16(p) = p (1 + e), |e| <= 2^-8 (the unit roundoff of
+    an 8-bit significand), the P rounding moves O_i by at most
+    2^-8 sum_j p_ij |v_j| / l_i = 2^-8 (P|V|)_i, and the final rounding by half
+    a BF16 unit in the last place. FP32 accumulation and the exp2/log2 units
+    add relative errors near 1e-6. Hence
+        |O_gpu - O_ref| <= 0.5 ulp_bf16(|O_ref| (1 + 2^-7))
+                           + 1.125 * 2^-8 (P|V|)_ref + 1e-6,
+    where (P|V|)_ref is the oracle's attention output with V replaced by |V|.
+  * internal, aggregate: relative RMS error of O <= 2^-8.
+"""
+import numpy as np
+import torch
+
+O_MAX_ABS = 1e-2
+LSE_REL = 1e-3
+O_REL_RMS = 2.0 ** -8
+
+
+def have_gpu() -> bool:
+    return torch.cuda.is_available()
+
+
+def to_dev(bits: np.ndarray) -> torch.Tensor:
+    """BF16 bit pattern array (uint16) -> contiguous bfloat16 tensor on cuda:0."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.view(torch.bfloat16).to("cuda:0")
+
+
+def to_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of BF16 numbers at |x| (normal range; 8-bit significand)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(ax)) - 7)
+
+
+def elem_bound(o_ref: np.ndarray, pabs_ref: np.ndarray) -> np.ndarray:
+    return 0.5 * ulp_bf16(np.abs(o_ref) * (1 + 2.0 ** -7)) + 1.125 * 2.0 ** -8 * pabs_ref + 1e-6
+
+
+def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, pabs_ref: np.ndarray, what: str) -> dict:
+    err = np.abs(o_gpu - o_ref)
+    finite = bool(np.isfinite(o_gpu).all())
+    max_abs = float(err.max()) if err.size else 0.0
+    rel_rms = float(np.sqrt((err ** 2).sum() / max((o_ref ** 2).sum(), 1e-300))) if err.size else 0.0
+    worst = float((err / elem_bound(o_ref, pabs_ref)).max()) if err.size else 0.0
+    stats = {"max_abs": max_abs, "rel_rms": rel_rms, "elem_ratio": worst}
+    print(f"    {what}: {stats}", flush=True)
+    assert finite, f"{what}: non-finite O"
+    assert max_abs <= O_MAX_ABS, f"{what}: O max abs error {max_abs:.3e} > {O_MAX_ABS}"
+    assert rel_rms <= O_REL_RMS, f"{what}: O rel-RMS error {rel_rms:.3e} > {O_REL_RMS:.3e}"
+    assert worst <= 1.0, f"{what}: O element error {worst:.3f} x the derived element bound"
+    return stats
+
+
+def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str) -> float:
+    rel = np.abs(lse_gpu - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+    worst = float(rel.max()) if rel.size else 0.0
+    print(f"    {what}: lse rel {worst:.3e}", flush=True)
+    assert np.isfinite(lse_gpu).all(), f"{what}: non-finite lse"
+    assert worst <= LSE_REL, f"{what}: lse relative error {worst:.3e} > {LSE_REL}"
+    return worst

@@ -1,0 +1,97 @@
+"""The C-ABI library loads, exports every symbol include/fa.h declares, and
+rejects bad arguments on the host before any HIP call (safe without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+LIB = os.path.join(ROOT, "exact_tiled_attention_fa_amd", "libfa.so")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(LIB), reason="libfa.so not built (run __graft_entry__.build())")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_]+\s*\*?\s*(fa_[a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from exact_tiled_attention_fa_amd import _lib
+    return _lib.lib()
+
+
+def test_header_declares_the_abi():
+    assert _declared_functions() == ["fa_decode", "fa_decode_workspace_bytes", "fa_fwd", "fa_status_string"]
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    from exact_tiled_attention_fa_amd import _lib
+    for code, name in _lib.STATUS_NAMES.items():
+        assert lib.fa_status_string(code).decode().startswith(name)
+    assert lib.fa_status_string(12345) == b"unknown fa_status"
+
+
+# Fake, 16-byte aligned, never-dereferenced addresses: every call below fails its
+# host-side argument checks before touching the device.
+P = 0x10000
+BAD = 0x10008  # 8-byte aligned only
+
+
+def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0, scale=0.125):
+    return lib.fa_fwd(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(k=None), -1), (dict(v=None), -1), (dict(o=None), -1), (dict(lse=None), -1),
+    (dict(B=0), -2), (dict(Hq=0), -2), (dict(Hkv=-1), -2), (dict(N=0), -2),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(d=0), -3),
+    (dict(Hq=6, Hkv=4), -4),
+    (dict(q=BAD), -5), (dict(o=BAD), -5), (dict(lse=P + 2), -5),
+    (dict(causal=2), -8), (dict(scale=float("nan")), -8), (dict(scale=float("inf")), -8),
+    (dict(B=1 << 20, Hq=1 << 12, N=1 << 20), -2),
+])
+def test_fwd_rejects(lib, kw, status):
+    assert fwd(lib, **kw) == status
+
+
+def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4, scale=0.1, ws=P, wsb=1 << 30):
+    return lib.fa_decode(q, k, v, o, lse, B, Hq, Hkv, L, d, splits, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(lse=None), -1),
+    (dict(L=0), -2), (dict(splits=0), -2), (dict(splits=101), -2), (dict(B=0), -2),
+    (dict(d=32), -3), (dict(Hq=6, Hkv=4), -4),
+    (dict(k=BAD), -5), (dict(ws=BAD), -5),
+    (dict(scale=float("nan")), -8),
+    (dict(ws=None), -6), (dict(wsb=16), -6),
+])
+def test_decode_rejects(lib, kw, status):
+    assert dec(lib, **kw) == status
+
+
+def test_decode_workspace_size(lib):
+    # 16 x 32 rows, 16 chunks of 512 keys, (128 + 1) floats each.
+    assert lib.fa_decode_workspace_bytes(16, 32, 8192, 128, 16) == 16 * 32 * 16 * 129 * 4
+    # L = 5, 4 splits -> chunk 2 -> 3 non-empty chunks.
+    assert lib.fa_decode_workspace_bytes(1, 1, 5, 64, 4) == (3 * 65 * 4 + 255) // 256 * 256
+    assert lib.fa_decode_workspace_bytes(1, 1, 5, 64, 6) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, 5, 60, 1) == 0
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import exact_tiled_attention_fa_amd as fa
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        fa.fwd(x, x, x)

@@ -1,0 +1,115 @@
+"""GPU parity of the forward kernel against the FP64 oracle, through the C ABI.
+
+Every workload's inputs come from seeded_inputs (the same BF16 values reach the
+GPU and, widened exactly, the oracle). Large workloads are checked on a seeded
+sample of rows per head; the kernel always computes every row.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import seeded_inputs as si
+from gpu_helpers import check_lse, check_o, have_gpu, to_dev, to_f64
+from oracle import fa_oracle
+
+pytestmark = [pytest.mark.gpu, pytest.mark.skipif(not have_gpu(), reason="needs a GPU")]
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _run_case(case: si.FwdCase, scale=None):
+    import exact_tiled_attention_fa_amd as fa
+    scale = case.scale if scale is None else scale
+    _say(f"[fwd] {case.name} causal={case.causal} seed={case.seed} scale={scale}")
+    qb, kb, vb = si.fwd_inputs(case)
+    q, k, v = to_dev(qb), to_dev(kb), to_dev(vb)
+    o, lse = fa.fwd(q, k, v, causal=case.causal, scale=scale)
+    import torch
+    torch.cuda.synchronize()
+    o_np, lse_np = to_f64(o), to_f64(lse)
+    del q, k, v, o, lse
+    qf, kf, vf = si.bf16_bits_to_f32(qb), si.bf16_bits_to_f32(kb), si.bf16_bits_to_f32(vb)
+    if case.sampled_rows:
+        rows = np.stack([si.sample_rows(case.seed, h, case.N, case.sampled_rows) for h in range(case.Hq)])
+    else:
+        rows = None
+    # One oracle pass over [V, |V|]: O and the P|V| term of the element bound.
+    vx = np.concatenate([vf, np.abs(vf)], axis=-1)
+    ox_ref, lse_ref = fa_oracle.attention_ref(qf, kf, vx, case.causal, scale, rows=rows)
+    o_ref, pabs_ref = ox_ref[..., :case.d], ox_ref[..., case.d:]
+    del vx, ox_ref
+    if rows is not None:
+        o_np = np.stack([o_np[:, h, rows[h]] for h in range(case.Hq)], axis=1)
+        lse_np = np.stack([lse_np[:, h, rows[h]] for h in range(case.Hq)], axis=1)
+    stats = check_o(o_np, o_ref, pabs_ref, case.name)
+    stats["lse_rel"] = check_lse(lse_np, lse_ref, case.name)
+    return stats
+
+
+@pytest.mark.parametrize("case", [si.TINY, si.ONE_HEAD_8K, si.ONE_HEAD_8K_CAUSAL, si.HEADS32_4K,
+                                  si.HEADS32_4K_CAUSAL], ids=lambda c: c.name)
+def test_workloads(case):
+    _run_case(case)
+
+
+def test_long_context_128k_causal():
+    _run_case(si.LONG_128K)
+
+
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 1000])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_ragged_lengths(N, d, causal):
+    case = si.FwdCase(f"ragged N{N} d{d}", 2, 4, 2, N, d, causal, seed=1000 + N + d)
+    _run_case(case)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2, 0.5])
+def test_scale_edge_cases(scale):
+    for causal in (False, True):
+        case = si.FwdCase(f"scale {scale}", 1, 2, 1, 300, 128, causal, seed=77)
+        _run_case(case, scale=scale)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (6, 3), (4, 4), (8, 1)])
+def test_gqa_mapping(Hq, Hkv):
+    _run_case(si.FwdCase(f"gqa {Hq}/{Hkv}", 2, Hq, Hkv, 256, 64, True, seed=50 + Hq + Hkv))
+
+
+def test_run_to_run_bitwise_determinism():
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    case = si.FwdCase("determinism", 1, 8, 8, 2048, 128, False, seed=9)
+    q, k, v = (to_dev(x) for x in si.fwd_inputs(case))
+    o1, l1 = fa.fwd(q, k, v, causal=False)
+    o2, l2 = fa.fwd(q, k, v, causal=True)
+    o3, l3 = fa.fwd(q, k, v, causal=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o1.view(torch.int16), o3.view(torch.int16))
+    assert torch.equal(l1, l3)
+    assert not torch.equal(o1.view(torch.int16), o2.view(torch.int16))
+
+
+def test_equal_keys_give_mean_of_values_at_full_size():
+    """Property at the 8K size: identical keys make every weight 1/N (causal: 1/(i+1))."""
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    N, d = 8192, 128
+    rng = np.random.default_rng(31)
+    qb = si.normal_bf16(rng, (1, 1, N, d))
+    krow = si.normal_bf16(rng, (d,))
+    kb = np.broadcast_to(krow, (1, 1, N, d)).copy()
+    vb = si.normal_bf16(rng, (1, 1, N, d))
+    o, lse = fa.fwd(to_dev(qb), to_dev(kb), to_dev(vb), causal=True, scale=1 / math.sqrt(d))
+    torch.cuda.synchronize()
+    vf = si.bf16_bits_to_f32(vb)[0, 0].astype(np.float64)
+    prefix_mean = np.cumsum(vf, 0) / np.arange(1, N + 1)[:, None]
+    prefix_abs = np.cumsum(np.abs(vf), 0) / np.arange(1, N + 1)[:, None]
+    check_o(to_f64(o)[0, 0], prefix_mean, prefix_abs, "equal keys causal")
+    s = (si.bf16_bits_to_f32(qb)[0, 0].astype(np.float64) @ si.bf16_bits_to_f32(krow).astype(np.float64)) / math.sqrt(d)
+    check_lse(to_f64(lse)[0, 0], s + np.log(np.arange(1, N + 1)), "equal keys causal lse")
