@@ -10,9 +10,12 @@
 //
 // Mapping onto CDNA4:
 //   * 256 threads = 4 waves; each wave owns 32 query rows (128 per work-group).
-//   * K/V tiles of 64 keys are staged in LDS, double buffered: the next tile's
-//     global loads are issued before the current tile's math and written to
-//     the other buffer after it, so one barrier per tile suffices.
+//     Registers are budgeted for two work-groups per CU (two waves per SIMD),
+//     so one wave's softmax arithmetic overlaps the other's matrix products.
+//   * K/V tiles of 64 keys go HBM -> LDS with direct loads
+//     (global_load_lds_dwordx4: lane l of a wave fills bytes 16 l .. 16 l + 15
+//     of a 1 KiB block), double buffered; the loads of tile t+1 are issued
+//     before the math of tile t and waited for at the tile's closing barrier.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (A = K from LDS, B = Q^T held in registers for the whole sweep). In the
 //     result each lane holds 16 keys of ONE query row, so the row max and row
@@ -36,24 +39,22 @@ namespace fa {
 
 template <int D>
 struct FwdCfg {
-  static constexpr int CPR = D / 8;                         // 16-byte chunks per row
-  static constexpr int TILE_CHUNKS = kFwdKeys * CPR;        // chunks in one K or V tile
-  static constexpr int CPT = TILE_CHUNKS / kFwdThreads;     // chunks per thread per tile
-  static constexpr int KK = D / 16;                         // k-steps of S^T = K Q^T
-  static constexpr int DT = D / 32;                         // 32-wide d tiles of O^T
+  static constexpr int CPR = D / 8;                       // 16-byte chunks per K/V row
+  static constexpr int RPB = 64 / CPR;                    // rows per 1 KiB direct-load block
+  static constexpr int BLOCKS = kFwdKeys / RPB;           // 1 KiB blocks per K (or V) tile
+  static constexpr int BPW = BLOCKS / 4;                  // blocks per wave per tile
+  static constexpr int TILE_CHUNKS = kFwdKeys * CPR;
+  static constexpr int KK = D / 16;                       // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;                       // 32-wide d tiles of O^T
 };
 
-// LDS placement of 16-byte chunk `c` of tile row `r` (in chunks). The XOR
-// swizzles keep the two read patterns free of bank conflicts: K fragment reads
-// (32 rows, one chunk column) and V transposed reads (4 rows x 4 chunks).
+// XOR swizzles of the 16-byte chunk index within a tile row (in LDS). They keep
+// the two read patterns free of bank conflicts: K fragment reads (32 rows, one
+// chunk column) and V transposed reads (4 rows x 4 chunks per half wave).
 template <int D>
-__device__ __forceinline__ int k_slot(int r, int c) {
-  return D == 128 ? r * 16 + (c ^ (r & 15)) : r * 8 + (c ^ ((r >> 1) & 7));
-}
+__device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 template <int D>
-__device__ __forceinline__ int v_slot(int r, int c) {
-  return D == 128 ? r * 16 + (c ^ ((r & 3) << 2)) : r * 8 + (c ^ (((r >> 1) & 1) << 2));
-}
+__device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float a3) {
   __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1, b2 = (__bf16)a2, b3 = (__bf16)a3;
@@ -63,16 +64,24 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
   return r;
 }
 
+__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+}
+
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads) void fa_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  __shared__ uint4 lds_k[2][C::TILE_CHUNKS];
-  __shared__ uint4 lds_v[2][C::TILE_CHUNKS];
+  // Two static buffers per operand so the loop can name each one directly.
+  __shared__ uint4 k_lds0[C::TILE_CHUNKS];
+  __shared__ uint4 k_lds1[C::TILE_CHUNKS];
+  __shared__ uint4 v_lds0[C::TILE_CHUNKS];
+  __shared__ uint4 v_lds1[C::TILE_CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int g = lane >> 5;    // which half of the wave (k-slot group)
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;    // half of the wave (k-slot group)
   const int li = lane & 31;   // query row within the wave / column of S^T
 
   // ---- grid order: XCD-contiguous, head-major, heaviest query block first when causal
@@ -86,7 +95,30 @@ __global__ __launch_bounds__(kFwdThreads) void fa_fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int q0 = qb * kFwdRows;
   const size_t qo_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
-  const size_t kv_base = (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+  const uint16_t* kg = a.k + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+  const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+
+  const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
+  const int n_tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
+
+  // ---- direct HBM -> LDS loads of one K/V tile. Lane l fills physical chunk
+  // l % CPR of tile row r, which holds logical chunk (l % CPR) ^ swizzle(r).
+  // Rows past N are clamped to row N-1: finite data whose scores are masked.
+  const int dma_row = lane / C::CPR;
+  const int dma_p = lane % C::CPR;
+  auto issue_tile = [&](int kv0, uint4* kdst, uint4* vdst) {
+#pragma unroll
+    for (int x = 0; x < C::BPW; ++x) {
+      const int blk = wave * C::BPW + x;
+      const int r = blk * C::RPB + dma_row;
+      const int key = min(kv0 + r, N - 1);
+      dma16(kg + (size_t)key * D + 8 * (dma_p ^ kswz<D>(r)), kdst + blk * 64);
+      dma16(vg + (size_t)key * D + 8 * (dma_p ^ vswz<D>(r)), vdst + blk * 64);
+    }
+  };
+
+  // Tile 0's loads go out first; the Q fragments load while they fly.
+  issue_tile(0, k_lds0, v_lds0);
 
   // ---- Q^T operand of this lane's row, kept in registers for the whole sweep.
   // A negative scale is folded into Q (sign flip is exact), so the kernel
@@ -105,37 +137,21 @@ __global__ __launch_bounds__(kFwdThreads) void fa_fwd_kernel(FwdArgs a) {
     }
   }
 
-  const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
-  const int n_tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
-  const int wave_q0 = q0 + wave * 32;
-  const int wave_q1 = wave_q0 + 31;
-
-  uint4 kr[C::CPT], vr[C::CPT];
-  auto load_tile = [&](int kv0) {
+  // ---- per-lane LDS byte offsets (tile-relative). K: row li, chunk 2 kk + g.
+  // V^T: lane t16 of each 16-lane block names row t16 / 4 of a 4-key group and
+  // 4 columns at 32 dt + 16 vch + 4 (t16 % 4).
+  int koff[C::KK];
 #pragma unroll
-    for (int x = 0; x < C::CPT; ++x) {
-      const int idx = tid + x * kFwdThreads;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      const int key = kv0 + row;
-      if (key < N) {
-        const size_t off = kv_base + (size_t)key * D + ch * 8;
-        kr[x] = *reinterpret_cast<const uint4*>(a.k + off);
-        vr[x] = *reinterpret_cast<const uint4*>(a.v + off);
-      } else {
-        kr[x] = make_uint4(0u, 0u, 0u, 0u);
-        vr[x] = make_uint4(0u, 0u, 0u, 0u);
-      }
-    }
-  };
-  auto store_tile = [&](int buf) {
+  for (int kk = 0; kk < C::KK; ++kk) koff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ kswz<D>(li)));
+  const int t16 = lane & 15;
+  const int vch = (lane >> 4) & 1;
+  const int vrow = 4 * g + (t16 >> 2);  // + 32 jt + 16 hh (+ 8): multiples of 4 keep vswz fixed
+  int voff[C::DT];
 #pragma unroll
-    for (int x = 0; x < C::CPT; ++x) {
-      const int idx = tid + x * kFwdThreads;
-      const int row = idx / C::CPR, ch = idx % C::CPR;
-      lds_k[buf][k_slot<D>(row, ch)] = kr[x];
-      lds_v[buf][v_slot<D>(row, ch)] = vr[x];
-    }
-  };
+  for (int dt = 0; dt < C::DT; ++dt) {
+    const int chunk = (32 * dt + 16 * vch + 4 * (t16 & 3)) >> 3;
+    voff[dt] = 16 * (vrow * C::CPR + (chunk ^ vswz<D>(vrow))) + 8 * (t16 & 1);
+  }
 
   float m_run = -INFINITY;  // running max of t (base-2 scaled scores) for row qi
   float l_run = 0.f;        // running sum of 2^(t - m) over this lane's keys
@@ -143,106 +159,106 @@ __global__ __launch_bounds__(kFwdThreads) void fa_fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
 
-  // Lane-dependent parts of the V^T transposed-read addresses.
-  const int t16 = lane & 15;
-  const int vch = (lane >> 4) & 1;
+  const int wave_q0 = q0 + wave * 32;
+  const int wave_q1 = wave_q0 + 31;
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
+  auto tile_math = [&](int kv0, const uint4* kbuf, const uint4* vbuf) {
+    const char* kb = reinterpret_cast<const char*>(kbuf);
+    const char* vb = reinterpret_cast<const char*>(vbuf);
+    // ---- S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains interleave.
+    f32x16 s0 = f32x16{}, s1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
+      s0 = mfma32(k0, qf[kk], s0);
+      s1 = mfma32(k1, qf[kk], s1);
+    }
+    f32x16 s[2] = {s0, s1};
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * kFwdKeys;
-    const bool has_next = t + 1 < n_tiles;
-    if (has_next) load_tile(kv0 + kFwdKeys);
-    const int buf = t & 1;
-    if (!CAUSAL || kv0 <= wave_q1) {
-      const char* kb = reinterpret_cast<const char*>(lds_k[buf]);
-      const char* vb = reinterpret_cast<const char*>(lds_v[buf]);
-
-      // ---- S^T = K Q^T for two 32-key sub-tiles.
-      f32x16 s[2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt) {
-        s[jt] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < C::KK; ++kk) {
-          const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + 16 * k_slot<D>(jt * 32 + li, 2 * kk + g));
-          s[jt] = mfma32(kf, qf[kk], s[jt]);
-        }
-      }
-
-      // ---- online softmax; lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4 of row qi.
-      const bool need_mask = (kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0);
-      if (need_mask) {
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kv0 + jt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-            const bool ok = key < N && (!CAUSAL || key <= qi);
-            if (!ok) s[jt][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jt][r]);
-      mx = max_xor32(mx);
-      const float mt = mx == -INFINITY ? -INFINITY : mx * c;
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = exp2_hw(m_run - m_use);
-      m_run = m_new;
-      float rs = 0.f;
+    // ---- online softmax; lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4 of row qi.
+    const bool need_mask = (kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0);
+    if (need_mask) {
 #pragma unroll
       for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float p = exp2_hw(fmaf(s[jt][r], c, -m_use));
-          if (need_mask) p = s[jt][r] == -INFINITY ? 0.f : p;
-          s[jt][r] = p;
-          rs += p;
+          const int key = kv0 + jt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+          const bool ok = key < N && (!CAUSAL || key <= qi);
+          if (!ok) s[jt][r] = -INFINITY;
         }
-      l_run = fmaf(l_run, alpha, rs);
-      if (__any(alpha != 1.f)) {
-#pragma unroll
-        for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-      }
-
-      // ---- P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
-      //      32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
-      bf16x8 pb[2][2];
-#pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-          pb[jt][hh] = pack_bf16x8(s[jt][8 * hh + 0], s[jt][8 * hh + 1], s[jt][8 * hh + 2], s[jt][8 * hh + 3],
-                                   s[jt][8 * hh + 4], s[jt][8 * hh + 5], s[jt][8 * hh + 6], s[jt][8 * hh + 7]);
-
-      // ---- O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32
-      //      at the same 8 keys, gathered with two transposed reads of 4 keys each.
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt) {
-        const int col = 32 * dt + 16 * vch + 4 * (t16 & 3);
-        const int chunk = col >> 3;
-        const int half = (t16 & 1) * 8;
-#pragma unroll
-        for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int row0 = jt * 32 + 16 * hh + 4 * g + (t16 >> 2);
-            const i16x4 lo = lds_read_tr(vb + 16 * v_slot<D>(row0, chunk) + half);
-            const i16x4 hi = lds_read_tr(vb + 16 * v_slot<D>(row0 + 8, chunk) + half);
-            oacc[dt] = mfma32(join_bf16x8(lo, hi), pb[jt][hh], oacc[dt]);
-          }
-      }
     }
-    if (has_next) store_tile(buf ^ 1);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jt][r]);
+    mx = max_xor32(mx);
+    const float mt = mx == -INFINITY ? -INFINITY : mx * c;
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = exp2_hw(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float p = exp2_hw(fmaf(s[jt][r], c, -m_use));
+        if (need_mask) p = s[jt][r] == -INFINITY ? 0.f : p;
+        s[jt][r] = p;
+        rs += p;
+      }
+    l_run = fmaf(l_run, alpha, rs);
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+
+    // ---- P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
+    //      32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
+    bf16x8 pb[2][2];
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        pb[jt][hh] = pack_bf16x8(s[jt][8 * hh + 0], s[jt][8 * hh + 1], s[jt][8 * hh + 2], s[jt][8 * hh + 3],
+                                 s[jt][8 * hh + 4], s[jt][8 * hh + 5], s[jt][8 * hh + 6], s[jt][8 * hh + 7]);
+
+    // ---- O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32
+    //      at the same 8 keys, gathered with two transposed reads of 4 keys each.
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int rowoff = (32 * jt + 16 * hh) * C::CPR * 16;
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt) {
+          const i16x4 lo = lds_read_tr(vb + voff[dt] + rowoff);
+          const i16x4 hi = lds_read_tr(vb + voff[dt] + rowoff + 8 * C::CPR * 16);
+          oacc[dt] = mfma32(join_bf16x8(lo, hi), pb[jt][hh], oacc[dt]);
+        }
+      }
+  };
+
+  // ---- main loop, unrolled by two so each step names its buffers statically.
+  for (int t = 0; t < n_tiles; t += 2) {
+    const int kv0 = t * kFwdKeys;
+    // even step: math on buffer 0 while tile t+1 streams into buffer 1
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    if (t + 1 < n_tiles) issue_tile(kv0 + kFwdKeys, k_lds1, v_lds1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!CAUSAL || kv0 <= wave_q1) tile_math(kv0, k_lds0, v_lds0);
+    if (t + 1 >= n_tiles) break;
+    // odd step: math on buffer 1 while tile t+2 streams into buffer 0
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 2 < n_tiles) issue_tile(kv0 + 2 * kFwdKeys, k_lds0, v_lds0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (!CAUSAL || kv0 + kFwdKeys <= wave_q1) tile_math(kv0 + kFwdKeys, k_lds1, v_lds1);
   }
 
   // ---- epilogue: O = O / l (BF16, round to nearest even), lse = (m + log2 l) ln 2.
