@@ -14,6 +14,11 @@ algorithmic HBM GB/s (K and V read once per KV head).
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy kernel of known size, for
                                            normalising hardware byte counters)
+       python bench.py --only WORKLOAD [--reps R]
+                                          (one workload alone, for profilers:
+                                           fwd-1x1x8192, fwd-1x1x8192-causal,
+                                           fwd-1x32x4096, fwd-1x32x4096-causal,
+                                           fwd-1x8x131072-causal, decode)
 """
 from __future__ import annotations
 
@@ -73,6 +78,59 @@ def calibrate_copy() -> None:
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}), flush=True)
 
 
+def run_only(name: str, reps: int) -> None:
+    """Launch one workload `reps` times (after two warm-ups) and print its mean time."""
+    import numpy as np
+    import torch
+
+    import exact_tiled_attention_fa_amd as fa
+    import seeded_inputs as si
+
+    dev = torch.device("cuda:0")
+
+    def up(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    fwd_cases = {"fwd-1x1x8192": si.ONE_HEAD_8K, "fwd-1x1x8192-causal": si.ONE_HEAD_8K_CAUSAL,
+                 "fwd-1x32x4096": si.HEADS32_4K, "fwd-1x32x4096-causal": si.HEADS32_4K_CAUSAL,
+                 "fwd-1x8x131072-causal": si.LONG_128K}
+    if name in fwd_cases:
+        case = fwd_cases[name]
+        q, k, v = (up(x) for x in si.fwd_inputs(case))
+        o = torch.empty_like(q)
+        lse = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
+        fn = lambda: fa.fwd(q, k, v, causal=case.causal, scale=case.scale, out=o, lse=lse)  # noqa: E731
+        work = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
+        unit = "TFLOP/s"
+    elif name == "decode":
+        case = si.DECODE_GQA
+        q, k, v = (up(x) for x in si.decode_inputs(case))
+        ws = torch.empty(fa.decode_workspace_bytes(case.B, case.Hq, case.L, case.d, case.num_splits),
+                         dtype=torch.uint8, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
+        fn = lambda: fa.decode(q, k, v, num_splits=case.num_splits, scale=case.scale, workspace=ws,  # noqa: E731
+                               out=o, lse=lse)
+        work = 2.0 * case.B * case.Hkv * case.L * case.d * 2
+        unit = "GB/s"
+    else:
+        raise SystemExit(f"unknown workload {name}")
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    t = a.elapsed_time(b) * 1e-3 / reps
+    rate = work / t / (1e12 if unit == "TFLOP/s" else 1e9)
+    print(json.dumps({"workload": name, "reps": reps, "us": round(t * 1e6, 2), "rate": round(rate, 2),
+                      "unit": unit}), flush=True)
+
+
 def cpu_baseline(case, seconds: float) -> dict:
     """The FP64 oracle as it stands, timed on this host's cores over whole passes of the workload."""
     import numpy as np
@@ -110,6 +168,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary (non-step) measurements")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--only", default=None, help="run one workload alone (for profilers)")
+    ap.add_argument("--reps", type=int, default=5)
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +189,9 @@ def main() -> int:
         return 1
     if args.calibrate_copy:
         calibrate_copy()
+        return 0
+    if args.only:
+        run_only(args.only, args.reps)
         return 0
 
     dev = torch.device("cuda:0")

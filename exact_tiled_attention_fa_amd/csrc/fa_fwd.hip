@@ -15,7 +15,7 @@
 //   * K/V tiles of 64 keys go HBM -> LDS with direct loads
 //     (global_load_lds_dwordx4: lane l of a wave fills bytes 16 l .. 16 l + 15
 //     of a 1 KiB block), double buffered; the loads of tile t+1 are issued
-//     before the math of tile t and waited for at the tile's closing barrier.
+//     before the math of tile t and waited for at the next tile's barrier.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (A = K from LDS, B = Q^T held in registers for the whole sweep). In the
 //     result each lane holds 16 keys of ONE query row, so the row max and row
@@ -23,8 +23,10 @@
 //     registers, rounded to BF16, are directly the B operand (P^T) of the
 //     second product O^T = V^T P^T -- no LDS round trip for P.
 //   * V^T operands come from LDS with ds_read_b64_tr_b16 (transposed reads).
-//   * Softmax in base 2: t = s * scale * log2(e); p = 2^(t - m); the partial O
-//     is rescaled by 2^(m_old - m_new), skipped when no row's max moved.
+//   * Softmax in base 2: t = s * scale * log2(e); p = 2^(t - m). A row's
+//     reference max m moves (and O and l are rescaled by 2^(m_old - m_new))
+//     only when a tile's max exceeds it by more than 8, so most tiles skip the
+//     rescale; the result is the same for any reference.
 //   * Causal: K/V tiles past the block's last row are never loaded; a wave
 //     skips the math of tiles wholly above its rows; only the diagonal tiles
 //     (and a ragged tail) take the masked path.
@@ -68,15 +70,17 @@ __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
 }
 
+// The reference max of a row moves only when a tile's max exceeds it by more
+// than this many base-2 units; until then p = 2^(t - m) <= 2^8, and O and l are
+// rescaled together when it does move, so O / l and m + log2 l are unchanged.
+constexpr float kRescaleSlack = 8.f;
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D>;
-  // Two static buffers per operand so the loop can name each one directly.
-  __shared__ uint4 k_lds0[C::TILE_CHUNKS];
-  __shared__ uint4 k_lds1[C::TILE_CHUNKS];
-  __shared__ uint4 v_lds0[C::TILE_CHUNKS];
-  __shared__ uint4 v_lds1[C::TILE_CHUNKS];
+  __shared__ uint4 k_lds[2][C::TILE_CHUNKS];
+  __shared__ uint4 v_lds[2][C::TILE_CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -101,31 +105,42 @@ void fa_fwd_kernel(FwdArgs a) {
   const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
   const int n_tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
 
-  // ---- direct HBM -> LDS loads of one K/V tile. Lane l fills physical chunk
+  // ---- direct HBM -> LDS loads of one K or V tile. Lane l fills physical chunk
   // l % CPR of tile row r, which holds logical chunk (l % CPR) ^ swizzle(r).
   // Rows past N are clamped to row N-1: finite data whose scores are masked.
   const int dma_row = lane / C::CPR;
   const int dma_p = lane % C::CPR;
-  auto issue_tile = [&](int kv0, uint4* kdst, uint4* vdst) {
+  auto issue_k = [&](int tile, uint4* dst) {
 #pragma unroll
     for (int x = 0; x < C::BPW; ++x) {
       const int blk = wave * C::BPW + x;
       const int r = blk * C::RPB + dma_row;
-      const int key = min(kv0 + r, N - 1);
-      dma16(kg + (size_t)key * D + 8 * (dma_p ^ kswz<D>(r)), kdst + blk * 64);
-      dma16(vg + (size_t)key * D + 8 * (dma_p ^ vswz<D>(r)), vdst + blk * 64);
+      const int key = min(tile * kFwdKeys + r, N - 1);
+      dma16(kg + (size_t)key * D + 8 * (dma_p ^ kswz<D>(r)), dst + blk * 64);
+    }
+  };
+  auto issue_v = [&](int tile, uint4* dst) {
+#pragma unroll
+    for (int x = 0; x < C::BPW; ++x) {
+      const int blk = wave * C::BPW + x;
+      const int r = blk * C::RPB + dma_row;
+      const int key = min(tile * kFwdKeys + r, N - 1);
+      dma16(vg + (size_t)key * D + 8 * (dma_p ^ vswz<D>(r)), dst + blk * 64);
     }
   };
 
   // Tile 0's loads go out first; the Q fragments load while they fly.
-  issue_tile(0, k_lds0, v_lds0);
+  issue_k(0, k_lds[0]);
+  issue_v(0, v_lds[0]);
 
   // ---- Q^T operand of this lane's row, kept in registers for the whole sweep.
   // A negative scale is folded into Q (sign flip is exact), so the kernel
-  // always works with c = |scale| log2(e) >= 0 and max(t) = c max(s).
+  // works with c = |scale| log2(e) > 0 and max(t) = c max(s). For scale 0 it
+  // uses the smallest normal float: every finite score then gives exactly
+  // p = 2^0 = 1, as scale 0 does, while masked (-inf) scores still give 0.
   const int qi = q0 + wave * 32 + li;
   const uint32_t sign = a.c < 0.f ? 0x80008000u : 0u;
-  const float c = fabsf(a.c);
+  const float c = fmaxf(fabsf(a.c), 1.17549435e-38f);
   bf16x8 qf[C::KK];
   {
     const uint4* qrow = reinterpret_cast<const uint4*>(a.q + qo_base + (size_t)(qi < N ? qi : 0) * D);
@@ -153,8 +168,8 @@ void fa_fwd_kernel(FwdArgs a) {
     voff[dt] = 16 * (vrow * C::CPR + (chunk ^ vswz<D>(vrow))) + 8 * (t16 & 1);
   }
 
-  float m_run = -INFINITY;  // running max of t (base-2 scaled scores) for row qi
-  float l_run = 0.f;        // running sum of 2^(t - m) over this lane's keys
+  float m_run = -INFINITY;  // reference max of t (base-2 scaled scores) for row qi
+  float l_run = 0.f;        // running sum of 2^(t - m_run) over this lane's keys
   f32x16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
@@ -162,11 +177,11 @@ void fa_fwd_kernel(FwdArgs a) {
   const int wave_q0 = q0 + wave * 32;
   const int wave_q1 = wave_q0 + 31;
 
-  auto tile_math = [&](int kv0, const uint4* kbuf, const uint4* vbuf) {
+  // S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains interleave.
+  auto scores = [&](const uint4* kbuf, f32x16& s0, f32x16& s1) {
     const char* kb = reinterpret_cast<const char*>(kbuf);
-    const char* vb = reinterpret_cast<const char*>(vbuf);
-    // ---- S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains interleave.
-    f32x16 s0 = f32x16{}, s1 = f32x16{};
+    s0 = f32x16{};
+    s1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
@@ -174,61 +189,65 @@ void fa_fwd_kernel(FwdArgs a) {
       s0 = mfma32(k0, qf[kk], s0);
       s1 = mfma32(k1, qf[kk], s1);
     }
-    f32x16 s[2] = {s0, s1};
+  };
 
-    // ---- online softmax; lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4 of row qi.
-    const bool need_mask = (kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0);
-    if (need_mask) {
+  // Keys outside the mask become -inf (only diagonal and ragged tiles need it).
+  // Key kv0 + o + 4 g (o = 32 jt + 8 (r/4) + r%4, a constant) is visible iff
+  // it is <= min(N-1, qi) (causal) or <= N-1, i.e. iff o <= lim.
+  auto apply_mask = [&](int kv0, f32x16& s0, f32x16& s1) {
+    const int lim = (CAUSAL ? min(N - 1, qi) : N - 1) - kv0 - 4 * g;
 #pragma unroll
-      for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = kv0 + jt * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-          const bool ok = key < N && (!CAUSAL || key <= qi);
-          if (!ok) s[jt][r] = -INFINITY;
-        }
+    for (int r = 0; r < 16; ++r) {
+      const int o = 8 * (r >> 2) + (r & 3);
+      if (o > lim) s0[r] = -INFINITY;
+      if (o + 32 > lim) s1[r] = -INFINITY;
     }
+  };
+
+  // Online softmax of one tile (lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4
+  // of row qi), then O^T += V^T P^T. With c > 0, a -inf score gives p = 0.
+  auto softmax_pv = [&](const uint4* vbuf, f32x16& s0, f32x16& s1) {
     float mx = -INFINITY;
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[jt][r]);
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
     mx = max_xor32(mx);
-    const float mt = mx == -INFINITY ? -INFINITY : mx * c;
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = exp2_hw(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
-#pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float p = exp2_hw(fmaf(s[jt][r], c, -m_use));
-        if (need_mask) p = s[jt][r] == -INFINITY ? 0.f : p;
-        s[jt][r] = p;
-        rs += p;
-      }
-    l_run = fmaf(l_run, alpha, rs);
-    if (__any(alpha != 1.f)) {
+    const float mt = mx * c;
+    const bool grow = mt > m_run + kRescaleSlack;
+    if (__any(grow)) {
+      const float m_new = grow ? mt : m_run;
+      const float alpha = exp2_hw(m_run - m_new);  // 1 for rows that keep their reference
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
     }
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float p0 = exp2_hw(fmaf(s0[r], c, nm));
+      const float p1 = exp2_hw(fmaf(s1[r], c, nm));
+      s0[r] = p0;
+      s1[r] = p1;
+      rs += p0 + p1;
+    }
+    l_run += rs;
 
-    // ---- P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
-    //      32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
+    // P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
+    // 32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
     bf16x8 pb[2][2];
 #pragma unroll
-    for (int jt = 0; jt < 2; ++jt)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-        pb[jt][hh] = pack_bf16x8(s[jt][8 * hh + 0], s[jt][8 * hh + 1], s[jt][8 * hh + 2], s[jt][8 * hh + 3],
-                                 s[jt][8 * hh + 4], s[jt][8 * hh + 5], s[jt][8 * hh + 6], s[jt][8 * hh + 7]);
-
-    // ---- O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32
-    //      at the same 8 keys, gathered with two transposed reads of 4 keys each.
+    for (int hh = 0; hh < 2; ++hh) {
+      pb[0][hh] = pack_bf16x8(s0[8 * hh + 0], s0[8 * hh + 1], s0[8 * hh + 2], s0[8 * hh + 3],
+                              s0[8 * hh + 4], s0[8 * hh + 5], s0[8 * hh + 6], s0[8 * hh + 7]);
+      pb[1][hh] = pack_bf16x8(s1[8 * hh + 0], s1[8 * hh + 1], s1[8 * hh + 2], s1[8 * hh + 3],
+                              s1[8 * hh + 4], s1[8 * hh + 5], s1[8 * hh + 6], s1[8 * hh + 7]);
+    }
+    // The V^T operand of lane l is column d = 32 dt + l%32 at the same 8 keys,
+    // gathered with two transposed reads of 4 keys each.
+    const char* vb = reinterpret_cast<const char*>(vbuf);
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -243,22 +262,21 @@ void fa_fwd_kernel(FwdArgs a) {
       }
   };
 
-  // ---- main loop, unrolled by two so each step names its buffers statically.
-  for (int t = 0; t < n_tiles; t += 2) {
+  // ---- main loop: the next tile streams into the other buffer during this tile's math.
+  for (int t = 0; t < n_tiles; ++t) {
     const int kv0 = t * kFwdKeys;
-    // even step: math on buffer 0 while tile t+1 streams into buffer 1
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) issue_tile(kv0 + kFwdKeys, k_lds1, v_lds1);
+    if (t + 1 < n_tiles) {
+      issue_k(t + 1, k_lds[(t + 1) & 1]);
+      issue_v(t + 1, v_lds[(t + 1) & 1]);
+    }
     __builtin_amdgcn_sched_barrier(0);
-    if (!CAUSAL || kv0 <= wave_q1) tile_math(kv0, k_lds0, v_lds0);
-    if (t + 1 >= n_tiles) break;
-    // odd step: math on buffer 1 while tile t+2 streams into buffer 0
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-    if (t + 2 < n_tiles) issue_tile(kv0 + 2 * kFwdKeys, k_lds0, v_lds0);
-    __builtin_amdgcn_sched_barrier(0);
-    if (!CAUSAL || kv0 + kFwdKeys <= wave_q1) tile_math(kv0 + kFwdKeys, k_lds1, v_lds1);
+    if (CAUSAL && kv0 > wave_q1) continue;  // every key of the tile is above this wave's rows
+    f32x16 s0, s1;
+    scores(k_lds[t & 1], s0, s1);
+    if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
+    softmax_pv(v_lds[t & 1], s0, s1);
   }
 
   // ---- epilogue: O = O / l (BF16, round to nearest even), lse = (m + log2 l) ln 2.
