@@ -3,6 +3,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fa.h"
 #include "fa_launch.h"
 
@@ -27,6 +29,25 @@ int decode_splits_used(int L, int num_splits) {
   const int chunk = decode_chunk(L, num_splits);
   return (L + chunk - 1) / chunk;
 }
+
+// Compute units of the current device (queried once per device).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  if (dev >= 0 && dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  if (dev >= 0 && dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Fewest key tiles a split may hold: shorter splits spend too much of their
+// time in the prologue and the partial-result write.
+constexpr int kMinSplitTiles = 8;
 
 int next_pow2_le16(int g) {
   int p = 1;
@@ -64,7 +85,9 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   if (elems(B, Hq, N, d) < 0) return FA_ERR_SHAPE;
   const int64_t nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
   const int64_t nwg = (int64_t)B * Hq * nqb;
-  if (nwg > INT32_MAX) return FA_ERR_SHAPE;
+  // Work-group count (also after a key split, which targets at most 2 per CU
+  // beyond this) and the combine's one-wave-per-row grid must fit the launch.
+  if (nwg > INT32_MAX / 4 || (int64_t)B * Hq * N > INT32_MAX) return FA_ERR_SHAPE;
 
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -75,9 +98,39 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N;
   a.c = scale * fa::kLog2eHost;
   a.nqb = (int)nqb;
-  a.nwg = (int)nwg;
-  const hipError_t e = fa::launch_fwd(a, d, causal != 0, reinterpret_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  a.o_part = nullptr;
+  a.lse_part = nullptr;
+
+  // Key split for grids that would leave CUs idle: aim at two work-groups per
+  // CU, never fewer than kMinSplitTiles key tiles per split.
+  const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
+  int n_splits = 1;
+  int split_tiles = tiles;
+  const int64_t target = 2 * (int64_t)device_cu_count();
+  if (nwg < target && tiles >= 2 * kMinSplitTiles) {
+    const int64_t want = (target + nwg - 1) / nwg;
+    n_splits = (int)(want < tiles / kMinSplitTiles ? want : tiles / kMinSplitTiles);
+    split_tiles = (tiles + n_splits - 1) / n_splits;
+    n_splits = (tiles + split_tiles - 1) / split_tiles;
+  }
+  a.n_splits = n_splits;
+  a.split_tiles = split_tiles;
+  a.nwg = (int)(nwg * n_splits);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (n_splits == 1) {
+    const hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
+    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+  }
+  const size_t rows = (size_t)B * Hq * N;
+  const size_t bytes = rows * n_splits * ((size_t)d + 1) * sizeof(float);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
+  a.o_part = static_cast<float*>(ws);
+  a.lse_part = a.o_part + rows * n_splits * d;
+  hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
+  if (e == hipSuccess) e = fa::launch_fwd_combine(a, d, causal != 0, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  return (e == hipSuccess && ef == hipSuccess) ? FA_OK : FA_ERR_LAUNCH;
 }
 
 extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits) {

@@ -88,10 +88,15 @@ void fa_fwd_kernel(FwdArgs a) {
   const int g = lane >> 5;    // half of the wave (k-slot group)
   const int li = lane & 31;   // query row within the wave / column of S^T
 
-  // ---- grid order: XCD-contiguous, head-major, heaviest query block first when causal
+  // ---- grid order: XCD-contiguous; head-major, then key split, then query
+  // block (heaviest first when causal), so the blocks sharing one K/V chunk sit
+  // together on one XCD.
   const int lid = xcd_contiguous(blockIdx.x, a.nwg);
-  const int bh = lid / a.nqb;
-  int qb = lid - bh * a.nqb;
+  const int per_head = a.nqb * a.n_splits;
+  const int bh = lid / per_head;
+  const int rem = lid - bh * per_head;
+  const int split = rem / a.nqb;
+  int qb = rem - split * a.nqb;
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
@@ -103,7 +108,9 @@ void fa_fwd_kernel(FwdArgs a) {
   const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
 
   const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
-  const int n_tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
+  const int t_begin = split * a.split_tiles;
+  const int n_tiles = min((kv_end + kFwdKeys - 1) / kFwdKeys, t_begin + a.split_tiles) - t_begin;
+  if (n_tiles <= 0) return;  // this split lies past the block's last visible key
 
   // ---- direct HBM -> LDS loads of one K or V tile. Lane l fills physical chunk
   // l % CPR of tile row r, which holds logical chunk (l % CPR) ^ swizzle(r).
@@ -115,7 +122,7 @@ void fa_fwd_kernel(FwdArgs a) {
     for (int x = 0; x < C::BPW; ++x) {
       const int blk = wave * C::BPW + x;
       const int r = blk * C::RPB + dma_row;
-      const int key = min(tile * kFwdKeys + r, N - 1);
+      const int key = min((t_begin + tile) * kFwdKeys + r, N - 1);
       dma16(kg + (size_t)key * D + 8 * (dma_p ^ kswz<D>(r)), dst + blk * 64);
     }
   };
@@ -124,7 +131,7 @@ void fa_fwd_kernel(FwdArgs a) {
     for (int x = 0; x < C::BPW; ++x) {
       const int blk = wave * C::BPW + x;
       const int r = blk * C::RPB + dma_row;
-      const int key = min(tile * kFwdKeys + r, N - 1);
+      const int key = min((t_begin + tile) * kFwdKeys + r, N - 1);
       dma16(vg + (size_t)key * D + 8 * (dma_p ^ vswz<D>(r)), dst + blk * 64);
     }
   };
@@ -264,7 +271,7 @@ void fa_fwd_kernel(FwdArgs a) {
 
   // ---- main loop: the next tile streams into the other buffer during this tile's math.
   for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = t * kFwdKeys;
+    const int kv0 = (t_begin + t) * kFwdKeys;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 1 < n_tiles) {
@@ -279,22 +286,74 @@ void fa_fwd_kernel(FwdArgs a) {
     softmax_pv(v_lds[t & 1], s0, s1);
   }
 
-  // ---- epilogue: O = O / l (BF16, round to nearest even), lse = (m + log2 l) ln 2.
+  // ---- epilogue: O = O / l, lse = (m + log2 l) ln 2. Unsplit: O rounded to
+  // BF16 (nearest even) straight to the output. Split: FP32 partials.
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  const float lse_v = l_tot > 0.f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
   if (qi < N) {
-    uint16_t* orow = a.o + qo_base + (size_t)qi * D;
+    const size_t row = (size_t)(b * a.Hq + h) * N + qi;
+    if (a.n_splits == 1) {
+      uint16_t* orow = a.o + qo_base + (size_t)qi * D;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+      for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const uint2 w = pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
-                                    oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-        *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * g) = w;
-      }
-    if (g == 0)
-      a.lse[(size_t)(b * a.Hq + h) * N + qi] = l_tot > 0.f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
+        for (int rq = 0; rq < 4; ++rq) {
+          const uint2 w = pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
+                                      oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
+          *reinterpret_cast<uint2*>(orow + 32 * dt + 8 * rq + 4 * g) = w;
+        }
+      if (g == 0) a.lse[row] = lse_v;
+    } else {
+      float* prow = a.o_part + (row * a.n_splits + split) * D;
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const float4 w = make_float4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
+                                       oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
+          *reinterpret_cast<float4*>(prow + 32 * dt + 8 * rq + 4 * g) = w;
+        }
+      if (g == 0) a.lse_part[row * a.n_splits + split] = lse_v;
+    }
   }
+}
+
+// One wave per row: merge the row's non-empty key splits with the
+// log-sum-exp combine (M = max lse_s, w_s = exp(lse_s - M),
+// O = sum w_s O_s / sum w_s, lse = M + ln sum w_s).
+template <int D, bool CAUSAL>
+__global__ __launch_bounds__(64) void fa_fwd_combine_kernel(FwdArgs a) {
+  constexpr int PER = D / 64;
+  const size_t row = blockIdx.x;
+  const int lane = threadIdx.x;
+  const int n = (int)(row % (size_t)a.N);
+  const int qb = n / kFwdRows;
+  const int kv_end = CAUSAL ? min(a.N, qb * kFwdRows + kFwdRows) : a.N;
+  const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
+  const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
+  const float* lp = a.lse_part + row * a.n_splits;
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  float wsum = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float w = exp2_hw((lp[s] - Ms) * kLog2e);
+    wsum += w;
+    const float* op = a.o_part + (row * a.n_splits + s) * D + lane * PER;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, op[j], acc[j]);
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const __bf16 bv = (__bf16)(acc[j] * inv);
+    a.o[row * D + lane * PER + j] = __builtin_bit_cast(uint16_t, bv);
+  }
+  if (lane == 0) a.lse[row] = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
 }
 
 template <int D, bool CAUSAL>
@@ -306,6 +365,18 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
   if (d == 128) return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
   return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
+}
+
+template <int D, bool CAUSAL>
+static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t stream) {
+  const unsigned rows = (unsigned)((size_t)a.B * a.Hq * a.N);
+  hipLaunchKernelGGL((fa_fwd_combine_kernel<D, CAUSAL>), dim3(rows), dim3(64), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  if (d == 128) return causal ? launch_combine_t<128, true>(a, stream) : launch_combine_t<128, false>(a, stream);
+  return causal ? launch_combine_t<64, true>(a, stream) : launch_combine_t<64, false>(a, stream);
 }
 
 }  // namespace fa

@@ -9,7 +9,12 @@ namespace fa {
 
 constexpr float kLog2eHost = 1.4426950408889634f;
 
-// Forward pass: one work-group per (batch, query head, 128-row query block).
+// Forward pass: one work-group per (batch, query head, key split, 128-row
+// query block). With n_splits == 1 each work-group sweeps all keys of its
+// block and writes O and lse; otherwise split s covers key tiles
+// [s * split_tiles, (s + 1) * split_tiles) and writes an FP32 normalised
+// partial O_s and its lse_s to o_part [B*Hq*N, n_splits, d] and
+// lse_part [B*Hq*N, n_splits] for fa_fwd_combine_kernel.
 struct FwdArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -20,12 +25,18 @@ struct FwdArgs {
   float c;   // scale * log2(e): scores are handled in base 2
   int nqb;   // query blocks per head
   int nwg;   // total work-groups
+  int n_splits;
+  int split_tiles;
+  float* o_part;
+  float* lse_part;
 };
 constexpr int kFwdRows = 128;     // query rows per work-group (4 waves x 32)
 constexpr int kFwdKeys = 64;      // keys per K/V tile
 constexpr int kFwdThreads = 256;
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+// Merge the key-split partials of a split forward into O (BF16) and lse.
+hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // Split-KV decode: one work-group per (batch, KV head, head group, chunk).
 struct DecArgs {

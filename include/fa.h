@@ -57,7 +57,7 @@ typedef enum {
 } fa_status;
 
 /*
- * fa_fwd -- attention forward pass (prefill), one kernel launch per call.
+ * fa_fwd -- attention forward pass (prefill).
  *
  *   q   [B, Hq,  N, d] bf16   queries
  *   k   [B, Hkv, N, d] bf16   keys
@@ -66,7 +66,15 @@ typedef enum {
  *   lse [B, Hq,  N]    fp32   natural-log logsumexp of each row's scaled scores
  *   causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
  *
- * d must be 64 or 128.
+ * d must be 64 or 128. One kernel launch per call, except when
+ * B * Hq * ceil(N / 128) work-groups would leave the GPU's compute units idle:
+ * then the keys of every query block are split across work-groups (at least
+ * 512 keys per split, about two work-groups per compute unit), each writing an
+ * FP32 normalised partial output and its logsumexp, and a second launch merges
+ * them with the log-sum-exp combine. That path takes a stream-ordered
+ * temporary buffer of B*Hq*N*splits*(d+1)*4 bytes from the device's default
+ * memory pool (hipMallocAsync / hipFreeAsync on `stream`) and returns
+ * FA_ERR_LAUNCH if the pool cannot supply it.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,

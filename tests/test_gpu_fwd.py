@@ -114,3 +114,10 @@ def test_equal_keys_give_mean_of_values_at_full_size():
     check_o(to_f64(o)[0, 0], prefix_mean, prefix_abs, "equal keys causal")
     s = (si.bf16_bits_to_f32(qb)[0, 0].astype(np.float64) @ si.bf16_bits_to_f32(krow).astype(np.float64)) / math.sqrt(d)
     check_lse(to_f64(lse)[0, 0], s + np.log(np.arange(1, N + 1)), "equal keys causal lse")
+
+
+@pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 4096, 128, False), (1, 2, 3000, 64, True),
+                                            (1, 1, 1100, 128, True), (2, 1, 2500, 128, False)])
+def test_key_split_path(B, H, N, d, causal):
+    """Grids of a few dozen work-groups take the key-split path (partials + combine)."""
+    _run_case(si.FwdCase(f"split B{B} H{H} N{N} d{d}", B, H, H, N, d, causal, seed=600 + N + d))
