@@ -6,10 +6,12 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   * forward on the same inputs, causal,
   * split-KV GQA decode: B = 16, Hq = 32, Hkv = 8, L = 8192, d = 128, 16 chunks.
 Inputs are seeded N(0,1) draws rounded to BF16 and resident in HBM before the
-timed region. `value` is the non-causal forward's algorithmic TFLOP/s
-(4 N^2 d per launch over the launch's average duration, measured with HIP
-events on the stream the kernel runs on). The decode rate is reported as
-algorithmic HBM GB/s (K and V read once per KV head).
+timed region, which runs K whole steps back to back (ms_per_step is its wall
+time per step). `value` is the non-causal forward's algorithmic TFLOP/s: 4 N^2 d
+per call over the call's average duration, measured with HIP events on the
+stream the kernels run on around K back-to-back calls (a call is the forward
+kernel, plus the combine kernel when the keys are split). The decode rate is
+reported as algorithmic HBM GB/s (K and V read once per KV head).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy kernel of known size, for
@@ -99,7 +101,7 @@ def run_only(name: str, reps: int) -> None:
         q, k, v = (up(x) for x in si.fwd_inputs(case))
         o = torch.empty_like(q)
         lse = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
-        fn = lambda: fa.fwd(q, k, v, causal=case.causal, scale=case.scale, out=o, lse=lse)  # noqa: E731
+        fn = fa.prepare_fwd(q, k, v, o, lse, causal=case.causal, scale=case.scale)
         work = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
         unit = "TFLOP/s"
     elif name == "decode":
@@ -109,8 +111,7 @@ def run_only(name: str, reps: int) -> None:
                          dtype=torch.uint8, device=dev)
         o = torch.empty_like(q)
         lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
-        fn = lambda: fa.decode(q, k, v, num_splits=case.num_splits, scale=case.scale, workspace=ws,  # noqa: E731
-                               out=o, lse=lse)
+        fn = fa.prepare_decode(q, k, v, o, lse, ws, num_splits=case.num_splits, scale=case.scale)
         work = 2.0 * case.B * case.Hkv * case.L * case.d * 2
         unit = "GB/s"
     else:
@@ -214,38 +215,40 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = {name: [] for name in ("fwd", "fwd_causal", "decode")}
+    # Argument checks happen once here; each launch then costs one C call.
+    run_fwd = fa.prepare_fwd(q, k, v, o, lse, causal=False, scale=fcase.scale)
+    run_fwd_c = fa.prepare_fwd(q, k, v, o_c, lse_c, causal=True, scale=fcase.scale)
+    run_dec = fa.prepare_decode(dq, dk, dv, do, dlse, ws, num_splits=dcase.num_splits, scale=dcase.scale)
 
-    def step(record: bool):
-        def timed(name, fn):
-            if record:
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                ev[name].append((a, b))
-            else:
-                fn()
-        timed("fwd", lambda: fa.fwd(q, k, v, causal=False, scale=fcase.scale, out=o, lse=lse))
-        timed("fwd_causal", lambda: fa.fwd(q, k, v, causal=True, scale=fcase.scale, out=o_c, lse=lse_c))
-        timed("decode", lambda: fa.decode(dq, dk, dv, num_splits=dcase.num_splits, scale=dcase.scale,
-                                          workspace=ws, out=do, lse=dlse))
+    def step():
+        run_fwd()
+        run_fwd_c()
+        run_dec()
 
     for _ in range(args.warmup):
-        step(False)
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / max(args.steps, 1)
 
-    def mean_s(name):
-        xs = [a.elapsed_time(b) for a, b in ev[name]]
-        return sum(xs) / len(xs) * 1e-3
+    # Per-operation call durations: HIP events on the launch stream around
+    # `steps` back-to-back calls of one operation (an event between every two
+    # launches would add its own gap to each interval).
+    def per_call_s(fn, reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(reps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e-3 / reps
 
-    t_fwd, t_fwd_c, t_dec = mean_s("fwd"), mean_s("fwd_causal"), mean_s("decode")
+    reps = max(args.steps, 1)
+    t_fwd, t_fwd_c, t_dec = per_call_s(run_fwd, reps), per_call_s(run_fwd_c, reps), per_call_s(run_dec, reps)
     flops = 4.0 * fcase.N * fcase.N * fcase.d
     tflops = flops / t_fwd / 1e12
     tflops_c = flops / 2 / t_fwd_c / 1e12
@@ -258,13 +261,14 @@ def main() -> int:
             q3, k3, v3 = (up(x) for x in si.fwd_inputs(case))
             o3 = torch.empty_like(q3)
             l3 = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
+            run3 = fa.prepare_fwd(q3, k3, v3, o3, l3, causal=case.causal, scale=case.scale)
             for _ in range(3):
-                fa.fwd(q3, k3, v3, causal=case.causal, out=o3, lse=l3)
+                run3()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 10
             a.record(stream)
             for _ in range(reps):
-                fa.fwd(q3, k3, v3, causal=case.causal, out=o3, lse=l3)
+                run3()
             b.record(stream)
             torch.cuda.synchronize()
             t = a.elapsed_time(b) * 1e-3 / reps

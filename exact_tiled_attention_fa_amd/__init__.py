@@ -16,7 +16,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "FaError"]
+__all__ = ["fwd", "decode", "decode_workspace_bytes", "prepare_fwd", "prepare_decode", "FaError"]
 
 
 def _stream_handle(device: torch.device) -> int:
@@ -93,3 +93,58 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 
                               workspace.numel() * workspace.element_size(), _stream_handle(q.device))
     _lib.check(st, "fa_decode")
     return out, lse
+
+
+def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                causal: bool = False, scale: float | None = None):
+    """Check the arguments once and return a callable that re-issues the same
+    forward with the least host work (one C call on the current stream).
+
+    The tensors must stay alive and unmoved while the callable is used.
+    """
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_bf16(name, t, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or out.shape != q.shape:
+        raise ValueError("shape mismatch between q, k, v and out")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = _lib.lib().fa_fwd
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale))
+    device = q.device
+
+    def call():
+        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        if st:
+            _lib.check(st, "fa_fwd")
+    return call
+
+
+def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                   workspace: torch.Tensor, num_splits: int = 16, scale: float | None = None):
+    """Like prepare_fwd, for split-KV decode with a caller-owned workspace."""
+    for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
+        _check_bf16(name, t, 4)
+    B, Hq, one, d = q.shape
+    Hkv, L = k.shape[1], k.shape[2]
+    if one != 1 or k.shape != (B, Hkv, L, d) or v.shape != k.shape or out.shape != q.shape:
+        raise ValueError("decode shapes: q,out [B,Hq,1,d], k,v [B,Hkv,L,d]")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    fn = _lib.lib().fa_decode
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+            B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size())
+    device = q.device
+
+    def call():
+        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        if st:
+            _lib.check(st, "fa_decode")
+    return call

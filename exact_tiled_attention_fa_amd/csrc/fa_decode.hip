@@ -46,8 +46,11 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Up to 4 query heads per group the kernel fits 128 VGPRs: four work-groups
+// per CU, so the workload's 2048 work-groups run in exactly two rounds.
 template <int D, int GM>
-__global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a) {
+__global__ __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_eu(GM <= 4 ? 4 : 2)))
+void fa_decode_split_kernel(DecArgs a) {
   using C = DecCfg<D>;
   __shared__ float p_lds[4][kDecWaveKeys][GM];
   __shared__ float alpha_lds[4][GM];
@@ -99,24 +102,21 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a)
 
   for (int kb = key_begin; kb < key_end; kb += kDecStepKeys) {
     const int kw = kb + wave * kDecWaveKeys;
-    // ---- loads: K in MFMA A layout, V coalesced
+    // ---- loads: K in MFMA A layout, V coalesced. Rows past the chunk read the
+    // chunk's last key instead (finite data): their scores become -inf, p = 0.
     bf16x8 kf[2][C::KK];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int key = kw + tt * 16 + n;
-      const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)(key < key_end ? key : key_begin) * D);
+      const int key = min(kw + tt * 16 + n, key_end - 1);
+      const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)key * D);
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) {
-        const uint4 w = key < key_end ? krow[4 * kk + quad] : make_uint4(0u, 0u, 0u, 0u);
-        kf[tt][kk] = __builtin_bit_cast(bf16x8, w);
-      }
+      for (int kk = 0; kk < C::KK; ++kk) kf[tt][kk] = __builtin_bit_cast(bf16x8, krow[4 * kk + quad]);
     }
     uint4 vr[C::NV];
 #pragma unroll
     for (int x = 0; x < C::NV; ++x) {
-      const int key = kw + rl + C::RPI * x;
-      vr[x] = key < key_end ? *reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)key * D + cl * 8)
-                            : make_uint4(0u, 0u, 0u, 0u);
+      const int key = min(kw + rl + C::RPI * x, key_end - 1);
+      vr[x] = *reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)key * D + cl * 8);
     }
 
     // ---- S^T tiles: lane holds head n, keys kw + 16 tt + 4 quad + r
@@ -225,37 +225,14 @@ __global__ __launch_bounds__(kDecThreads) void fa_decode_split_kernel(DecArgs a)
   }
 }
 
-// One wave per row: O = sum_c w_c O_c / sum_c w_c with w_c = exp(lse_c - max lse).
+// One wave per (sequence, query head): merge the chunks' partial results.
 template <int D>
 __global__ __launch_bounds__(64) void fa_combine_kernel(const float* __restrict__ o_part,
                                                         const float* __restrict__ lse_part,
                                                         uint16_t* __restrict__ o, float* __restrict__ lse,
                                                         int S) {
-  constexpr int PER = D / 64;
   const size_t row = blockIdx.x;
-  const int lane = threadIdx.x;
-  const float* lp = lse_part + row * S;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float wsum = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = exp2_hw((lp[s] - Ms) * kLog2e);
-    wsum += w;
-    const float* op = o_part + (row * S + s) * D + lane * PER;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, op[j], acc[j]);
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const __bf16 bv = (__bf16)(acc[j] * inv);
-    o[row * D + lane * PER + j] = __builtin_bit_cast(uint16_t, bv);
-  }
-  if (lane == 0) lse[row] = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+  combine_row<D>(o_part + row * S * D, lse_part + row * S, S, o + row * D, lse + row);
 }
 
 template <int D, int GM>

@@ -320,40 +320,16 @@ void fa_fwd_kernel(FwdArgs a) {
 }
 
 // One wave per row: merge the row's non-empty key splits with the
-// log-sum-exp combine (M = max lse_s, w_s = exp(lse_s - M),
-// O = sum w_s O_s / sum w_s, lse = M + ln sum w_s).
+// log-sum-exp combine.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void fa_fwd_combine_kernel(FwdArgs a) {
-  constexpr int PER = D / 64;
   const size_t row = blockIdx.x;
-  const int lane = threadIdx.x;
   const int n = (int)(row % (size_t)a.N);
   const int qb = n / kFwdRows;
   const int kv_end = CAUSAL ? min(a.N, qb * kFwdRows + kFwdRows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
   const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
-  const float* lp = a.lse_part + row * a.n_splits;
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float wsum = 0.f;
-  float acc[PER];
-#pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float w = exp2_hw((lp[s] - Ms) * kLog2e);
-    wsum += w;
-    const float* op = a.o_part + (row * a.n_splits + s) * D + lane * PER;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, op[j], acc[j]);
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const __bf16 bv = (__bf16)(acc[j] * inv);
-    a.o[row * D + lane * PER + j] = __builtin_bit_cast(uint16_t, bv);
-  }
-  if (lane == 0) a.lse[row] = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+  combine_row<D>(a.o_part + row * a.n_splits * D, a.lse_part + row * a.n_splits, S, a.o + row * D, a.lse + row);
 }
 
 template <int D, bool CAUSAL>
