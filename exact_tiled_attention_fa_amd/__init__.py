@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "decode", "decode_workspace_bytes", "prepare_fwd", "prepare_decode", "FaError"]
+__all__ = ["fwd", "decode", "fwd_workspace_bytes", "decode_workspace_bytes", "prepare_fwd", "prepare_decode",
+           "FaError"]
 
 
 def _stream_handle(device: torch.device) -> int:
@@ -63,6 +64,11 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
     return out, lse
 
 
+def fwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
+    """Workspace fa_fwd_ws needs on the current device (0: single launch)."""
+    return int(_lib.lib().fa_fwd_workspace_bytes(B, Hq, N, d))
+
+
 def decode_workspace_bytes(B: int, Hq: int, L: int, d: int, num_splits: int) -> int:
     return int(_lib.lib().fa_decode_workspace_bytes(B, Hq, L, d, num_splits))
 
@@ -98,7 +104,8 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 
 def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
                 causal: bool = False, scale: float | None = None):
     """Check the arguments once and return a callable that re-issues the same
-    forward with the least host work (one C call on the current stream).
+    forward with the least host work: one C call (fa_fwd_ws) on the current
+    stream, with a workspace allocated here once when the keys are split.
 
     The tensors must stay alive and unmoved while the callable is used.
     """
@@ -112,15 +119,18 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    fn = _lib.lib().fa_fwd
+    fn = _lib.lib().fa_fwd_ws
+    need = fwd_workspace_bytes(B, Hq, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale))
+            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), ws.data_ptr() if ws is not None else None, need)
     device = q.device
 
     def call():
         st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
         if st:
-            _lib.check(st, "fa_fwd")
+            _lib.check(st, "fa_fwd_ws")
+    call.workspace = ws  # keeps the buffer alive with the callable
     return call
 
 

@@ -33,6 +33,10 @@ def _declare(lib):
     vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_fwd.restype = i
+    lib.fa_fwd_workspace_bytes.argtypes = [i, i, i, i]
+    lib.fa_fwd_workspace_bytes.restype = sz
+    lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_fwd_ws.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]

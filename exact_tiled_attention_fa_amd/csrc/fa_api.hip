@@ -72,9 +72,11 @@ extern "C" const char* fa_status_string(int status) {
   }
 }
 
-extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
-                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
-                      fa_stream_t stream) {
+namespace {
+
+// Checks shared by the forward entry points; FA_OK or the failing status.
+int check_fwd_args(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || N <= 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -82,13 +84,52 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   if (causal != 0 && causal != 1) return FA_ERR_ARG;
   if (!isfinite(scale)) return FA_ERR_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse)) return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+// Sizes only: FA_OK or FA_ERR_SHAPE. The work-group count (also after a key
+// split, which targets at most two per CU beyond it) and the combine's
+// one-wave-per-row grid must fit a launch.
+int check_fwd_sizes(int B, int Hq, int N, int d) {
+  if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return FA_ERR_SHAPE;
   if (elems(B, Hq, N, d) < 0) return FA_ERR_SHAPE;
   const int64_t nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
-  const int64_t nwg = (int64_t)B * Hq * nqb;
-  // Work-group count (also after a key split, which targets at most 2 per CU
-  // beyond this) and the combine's one-wave-per-row grid must fit the launch.
-  if (nwg > INT32_MAX / 4 || (int64_t)B * Hq * N > INT32_MAX) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq * nqb > INT32_MAX / 4 || (int64_t)B * Hq * N > INT32_MAX) return FA_ERR_SHAPE;
+  return FA_OK;
+}
 
+struct FwdPlan {
+  int nqb, n_splits, split_tiles;
+  int64_t nwg;       // work-groups of the forward launch
+  size_t ws_bytes;   // partial-result buffer for a split, 0 otherwise
+};
+
+// Key split for grids that would leave CUs idle: aim at two work-groups per
+// CU, never fewer than kMinSplitTiles key tiles per split.
+FwdPlan plan_fwd(int B, int Hq, int N, int d) {
+  FwdPlan p;
+  p.nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
+  const int64_t base = (int64_t)B * Hq * p.nqb;
+  const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
+  p.n_splits = 1;
+  p.split_tiles = tiles;
+  const int64_t target = 2 * (int64_t)device_cu_count();
+  if (base < target && tiles >= 2 * kMinSplitTiles) {
+    const int64_t want = (target + base - 1) / base;
+    p.n_splits = (int)(want < tiles / kMinSplitTiles ? want : tiles / kMinSplitTiles);
+    p.split_tiles = (tiles + p.n_splits - 1) / p.n_splits;
+    p.n_splits = (tiles + p.split_tiles - 1) / p.split_tiles;
+  }
+  p.nwg = base * p.n_splits;
+  const size_t rows = (size_t)B * Hq * N;
+  const size_t bytes = p.n_splits > 1 ? rows * p.n_splits * ((size_t)d + 1) * sizeof(float) : 0;
+  p.ws_bytes = (bytes + 255) & ~(size_t)255;
+  return p;
+}
+
+int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* ws,
+                       hipStream_t s) {
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -97,40 +138,53 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N;
   a.c = scale * fa::kLog2eHost;
-  a.nqb = (int)nqb;
-  a.o_part = nullptr;
-  a.lse_part = nullptr;
-
-  // Key split for grids that would leave CUs idle: aim at two work-groups per
-  // CU, never fewer than kMinSplitTiles key tiles per split.
-  const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
-  int n_splits = 1;
-  int split_tiles = tiles;
-  const int64_t target = 2 * (int64_t)device_cu_count();
-  if (nwg < target && tiles >= 2 * kMinSplitTiles) {
-    const int64_t want = (target + nwg - 1) / nwg;
-    n_splits = (int)(want < tiles / kMinSplitTiles ? want : tiles / kMinSplitTiles);
-    split_tiles = (tiles + n_splits - 1) / n_splits;
-    n_splits = (tiles + split_tiles - 1) / split_tiles;
-  }
-  a.n_splits = n_splits;
-  a.split_tiles = split_tiles;
-  a.nwg = (int)(nwg * n_splits);
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  if (n_splits == 1) {
-    const hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
-    return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
-  }
-  const size_t rows = (size_t)B * Hq * N;
-  const size_t bytes = rows * n_splits * ((size_t)d + 1) * sizeof(float);
-  void* ws = nullptr;
-  if (hipMallocAsync(&ws, bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
+  a.nqb = p.nqb;
+  a.nwg = (int)p.nwg;
+  a.n_splits = p.n_splits;
+  a.split_tiles = p.split_tiles;
   a.o_part = static_cast<float*>(ws);
-  a.lse_part = a.o_part + rows * n_splits * d;
+  a.lse_part = ws ? a.o_part + (size_t)B * Hq * N * p.n_splits * d : nullptr;
   hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
-  if (e == hipSuccess) e = fa::launch_fwd_combine(a, d, causal != 0, s);
+  if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, d, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d) {
+  if (check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
+  return plan_fwd(B, Hq, N, d).ws_bytes;
+}
+
+extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                         void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                            p.ws_bytes > 0 ? workspace : nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                      int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                      fa_stream_t stream) {
+  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.ws_bytes == 0) return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, nullptr, s);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
+  st = launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, s);
   const hipError_t ef = hipFreeAsync(ws, s);
-  return (e == hipSuccess && ef == hipSuccess) ? FA_OK : FA_ERR_LAUNCH;
+  return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
 }
 
 extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits) {

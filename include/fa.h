@@ -81,6 +81,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            fa_stream_t stream);
 
 /*
+ * fa_fwd_workspace_bytes -- bytes of caller-provided workspace that fa_fwd_ws
+ * needs for these sizes on the current device: 0 when the forward runs as one
+ * launch, else the key-split partials (FP32 [B*Hq*N, splits, d] followed by
+ * FP32 [B*Hq*N, splits]) rounded up to 256 bytes. Returns 0 for invalid sizes.
+ */
+size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d);
+
+/*
+ * fa_fwd_ws -- fa_fwd with a caller-owned workspace instead of the
+ * stream-ordered temporary buffer: same operation, arguments and layouts, plus
+ * workspace / workspace_bytes (device memory, 16-byte aligned, at least
+ * fa_fwd_workspace_bytes(B, Hq, N, d); may be NULL when that is 0; contents on
+ * entry are ignored). Calls sharing a workspace must be ordered.
+ */
+int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
+              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+              void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
  * fa_decode_workspace_bytes -- size of the caller-provided workspace that
  * fa_decode needs for these sizes: FP32 partial outputs [B, Hq, S, d] and
  * partial logsumexps [B, Hq, S], S = number of non-empty chunks. Returns 0 for

@@ -26,7 +26,8 @@ def lib():
 
 
 def test_header_declares_the_abi():
-    assert _declared_functions() == ["fa_decode", "fa_decode_workspace_bytes", "fa_fwd", "fa_status_string"]
+    assert _declared_functions() == ["fa_decode", "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_workspace_bytes",
+                                     "fa_fwd_ws", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -62,6 +63,25 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd_ws(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0, scale=0.125, ws=P, wsb=0):
+    return lib.fa_fwd_ws(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(N=0), -2), (dict(d=80), -3), (dict(Hq=3, Hkv=2), -4),
+    (dict(v=BAD), -5), (dict(causal=-1), -8), (dict(scale=float("-inf")), -8),
+])
+def test_fwd_ws_rejects(lib, kw, status):
+    assert fwd_ws(lib, **kw) == status
+
+
+def test_fwd_workspace_size_rules(lib):
+    assert lib.fa_fwd_workspace_bytes(1, 1, 8192, 128) % 256 == 0
+    assert lib.fa_fwd_workspace_bytes(0, 1, 128, 128) == 0
+    assert lib.fa_fwd_workspace_bytes(1, 1, 128, 96) == 0
+    assert lib.fa_fwd_workspace_bytes(1, 1, 960, 128) == 0  # 15 key tiles: never split
 
 
 def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4, scale=0.1, ws=P, wsb=1 << 30):
