@@ -7,7 +7,8 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   * split-KV GQA decode: B = 16, Hq = 32, Hkv = 8, L = 8192, d = 128, 16 chunks.
 Inputs are seeded N(0,1) draws rounded to BF16 and resident in HBM before the
 timed region, which runs K whole steps back to back (ms_per_step is its wall
-time per step). `value` is the non-causal forward's algorithmic TFLOP/s: 4 N^2 d
+time per step). Before the W warm-up steps the step runs untimed for 0.5 s so
+the clock and address translation reach steady state. `value` is the non-causal forward's algorithmic TFLOP/s: 4 N^2 d
 per call over the call's average duration, measured with HIP events on the
 stream the kernels run on around K back-to-back calls (a call is the forward
 kernel, plus the combine kernel when the keys are split). The decode rate is
@@ -17,7 +18,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy kernel of known size, for
                                            normalising hardware byte counters)
        python bench.py --only WORKLOAD [--reps R]
-                                          (one workload alone, for profilers:
+                                          (one workload alone after a 0.5 s
+                                           untimed settle, for profilers:
                                            fwd-1x1x8192, fwd-1x1x8192-causal,
                                            fwd-1x32x4096, fwd-1x32x4096-causal,
                                            fwd-1x8x131072-causal, decode)
@@ -68,6 +70,19 @@ def measured_traffic():
         return None
 
 
+SETTLE_S = 0.5
+
+
+def settle(fn, seconds: float = SETTLE_S) -> None:
+    """Run `fn` untimed, synchronising every 16 calls, until `seconds` have passed."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(16):
+            fn()
+        torch.cuda.synchronize()
+
+
 def calibrate_copy() -> None:
     import torch
     n = 256 << 20
@@ -116,9 +131,7 @@ def run_only(name: str, reps: int) -> None:
         unit = "GB/s"
     else:
         raise SystemExit(f"unknown workload {name}")
-    for _ in range(2):
-        fn()
-    torch.cuda.synchronize()
+    settle(fn)
     stream = torch.cuda.current_stream(dev)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
@@ -225,6 +238,11 @@ def main() -> int:
         run_fwd_c()
         run_dec()
 
+    # Settle: run the step untimed for at least SETTLE_S seconds (the shader
+    # clock and address translation take milliseconds to reach steady state;
+    # a cold GPU runs the first millisecond of work up to 20% slower), then
+    # the W warm-up steps.
+    settle(step)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -262,8 +280,7 @@ def main() -> int:
             o3 = torch.empty_like(q3)
             l3 = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
             run3 = fa.prepare_fwd(q3, k3, v3, o3, l3, causal=case.causal, scale=case.scale)
-            for _ in range(3):
-                run3()
+            settle(run3, 0.2)
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             reps = 10
             a.record(stream)
