@@ -66,8 +66,24 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
   return r;
 }
 
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// fills bytes 16 l .. 16 l + 15 of the 1 KiB block at lds_dst, whose LDS
+// address goes in M0. Issued through inline assembly so that the compiler's
+// wait-count pass, which cannot tell which LDS buffer a direct load writes,
+// does not make the current tile's LDS reads wait for the next tile's loads;
+// the kernel waits for them itself (s_waitcnt vmcnt(0)) before the barrier
+// that hands the buffer to its readers. M0 is saved and restored around it.
 __device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_dst, 16, 0, 0);
+  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)lds_dst);
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(src)
+      : "memory");
 }
 
 // The reference max of a row moves only when a tile's max exceeds it by more
