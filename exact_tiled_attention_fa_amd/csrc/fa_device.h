@@ -49,10 +49,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // log2(x) (v_log_f32).
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// IEEE 754-2019 maximum (NaN-propagating). Unlike fmaxf it needs no quieting
+// of its operands, and chains max(max(a, b), c) become one v_maximum3_f32.
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 // Value of x in the lane 32 away (l ^ 32), combined with the own value.
 __device__ __forceinline__ float max_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return fmax_ieee(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_xor32(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

@@ -34,6 +34,8 @@
 //     a head adjacent (heaviest first when causal), and logical ids laid out so
 //     that each XCD gets one contiguous range: a head's K/V is then shared in
 //     one XCD's L2.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -67,24 +69,31 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
 }
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// fills bytes 16 l .. 16 l + 15 of the 1 KiB block at lds_dst, whose LDS
-// address goes in M0. Issued through inline assembly so that the compiler's
-// wait-count pass, which cannot tell which LDS buffer a direct load writes,
-// does not make the current tile's LDS reads wait for the next tile's loads;
-// the kernel waits for them itself (s_waitcnt vmcnt(0)) before the barrier
-// that hands the buffer to its readers. M0 is saved and restored around it.
-__device__ __forceinline__ void dma16(const void* src, void* lds_dst) {
-  const uint32_t lds = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)lds_dst);
+// fills bytes 16 l .. 16 l + 15 of the 1 KiB block whose LDS address goes in
+// M0; the global address is the uniform base plus the lane's 32-bit offset.
+// Issued through inline assembly so that the compiler's wait-count pass, which
+// cannot tell which LDS buffer a direct load writes, does not make LDS reads of
+// the other buffer wait for it; the kernel waits for its loads itself
+// (s_waitcnt vmcnt(0)) before the barrier that hands a buffer to its readers.
+// M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
   uint32_t saved;
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, off\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
-      : "s"(lds), "v"(src)
+      : "s"(lds), "v"(voff), "s"(base)
       : "memory");
 }
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // The reference max of a row moves only when a tile's max exceeds it by more
 // than this many base-2 units; until then p = 2^(t - m) <= 2^8, and O and l are
@@ -120,41 +129,52 @@ void fa_fwd_kernel(FwdArgs a) {
   const int N = a.N;
   const int q0 = qb * kFwdRows;
   const size_t qo_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
-  const uint16_t* kg = a.k + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
-  const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+  const int t_begin = split * a.split_tiles;
+  const uint16_t* kg = a.k + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
+  const uint16_t* vg = a.v + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
+  const int n_keys = N - t_begin * kFwdKeys;  // keys from the split's first one to the end
 
   const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
-  const int t_begin = split * a.split_tiles;
   const int n_tiles = min((kv_end + kFwdKeys - 1) / kFwdKeys, t_begin + a.split_tiles) - t_begin;
   if (n_tiles <= 0) return;  // this split lies past the block's last visible key
 
+  // Every wave takes every tile of its block; with causal masking the last
+  // tile of a block can be wholly above the rows of its first waves, whose
+  // scores there are all masked (p = 0).
+  const int wave_q0 = q0 + wave * 32;
+
   // ---- direct HBM -> LDS loads of one K or V tile. Lane l fills physical chunk
-  // l % CPR of tile row r, which holds logical chunk (l % CPR) ^ swizzle(r).
-  // Rows past N are clamped to row N-1: finite data whose scores are masked.
+  // l % CPR of tile row r, which holds logical chunk (l % CPR) ^ swizzle(r); the
+  // byte offsets from the tile's first row are fixed per lane. In a tile that
+  // runs past the last key, rows past it are clamped to it: finite data whose
+  // scores are masked.
   const int dma_row = lane / C::CPR;
   const int dma_p = lane % C::CPR;
-  auto issue_k = [&](int tile, uint4* dst) {
+  uint32_t kdo[C::BPW], vdo[C::BPW];
 #pragma unroll
-    for (int x = 0; x < C::BPW; ++x) {
-      const int blk = wave * C::BPW + x;
-      const int r = blk * C::RPB + dma_row;
-      const int key = min((t_begin + tile) * kFwdKeys + r, N - 1);
-      dma16(kg + (size_t)key * D + 8 * (dma_p ^ kswz<D>(r)), dst + blk * 64);
-    }
-  };
-  auto issue_v = [&](int tile, uint4* dst) {
+  for (int x = 0; x < C::BPW; ++x) {
+    const int r = (wave * C::BPW + x) * C::RPB + dma_row;
+    kdo[x] = 2u * (uint32_t)(r * D + 8 * (dma_p ^ kswz<D>(r)));
+    vdo[x] = 2u * (uint32_t)(r * D + 8 * (dma_p ^ vswz<D>(r)));
+  }
+  auto issue = [&](const uint16_t* src, const uint32_t* offs, bool is_v, int tile, uint4* dst) {
+    const uint16_t* base = src + (size_t)tile * kFwdKeys * D;
+    const int rows = n_keys - tile * kFwdKeys;
+    const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(wave * C::BPW);
+    if (rows >= kFwdKeys) {
 #pragma unroll
-    for (int x = 0; x < C::BPW; ++x) {
-      const int blk = wave * C::BPW + x;
-      const int r = blk * C::RPB + dma_row;
-      const int key = min((t_begin + tile) * kFwdKeys + r, N - 1);
-      dma16(vg + (size_t)key * D + 8 * (dma_p ^ vswz<D>(r)), dst + blk * 64);
+      for (int x = 0; x < C::BPW; ++x) dma16(base, offs[x], l0 + 1024u * x);
+    } else {
+#pragma unroll
+      for (int x = 0; x < C::BPW; ++x) {
+        const int r = (wave * C::BPW + x) * C::RPB + dma_row;
+        const int sw = is_v ? vswz<D>(r) : kswz<D>(r);
+        dma16(base, 2u * (uint32_t)(min(r, rows - 1) * D + 8 * (dma_p ^ sw)), l0 + 1024u * x);
+      }
     }
   };
 
-  // Tile 0's loads go out first; the Q fragments load while they fly.
-  issue_k(0, k_lds[0]);
-  issue_v(0, v_lds[0]);
+  issue(kg, kdo, false, 0, k_lds[0]);
 
   // ---- Q^T operand of this lane's row, kept in registers for the whole sweep.
   // A negative scale is folded into Q (sign flip is exact), so the kernel
@@ -196,13 +216,10 @@ void fa_fwd_kernel(FwdArgs a) {
   f32x16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
-
-  const int wave_q0 = q0 + wave * 32;
-  const int wave_q1 = wave_q0 + 31;
+  bf16x8 pb[2][2];          // P^T of the previous tile (BF16), consumed one step later
 
   // S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains interleave.
-  auto scores = [&](const uint4* kbuf, f32x16& s0, f32x16& s1) {
-    const char* kb = reinterpret_cast<const char*>(kbuf);
+  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1) {
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
@@ -211,6 +228,13 @@ void fa_fwd_kernel(FwdArgs a) {
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
       s0 = mfma32(k0, qf[kk], s0);
       s1 = mfma32(k1, qf[kk], s1);
+    }
+    // Reads run three k-steps ahead of the products.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      if (kk + 3 < C::KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
   };
 
@@ -227,50 +251,33 @@ void fa_fwd_kernel(FwdArgs a) {
     }
   };
 
-  // Online softmax of one tile (lane holds keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4
-  // of row qi), then O^T += V^T P^T. With c > 0, a -inf score gives p = 0.
-  auto softmax_pv = [&](const uint4* vbuf, f32x16& s0, f32x16& s1) {
-    float mx = -INFINITY;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-    mx = max_xor32(mx);
-    const float mt = mx * c;
-    const bool grow = mt > m_run + kRescaleSlack;
-    if (__any(grow)) {
-      const float m_new = grow ? mt : m_run;
-      const float alpha = exp2_hw(m_run - m_new);  // 1 for rows that keep their reference
-      m_run = m_new;
-      l_run *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
-    }
-    const float nm = m_run == -INFINITY ? 0.f : -m_run;
-    float rs = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const float p0 = exp2_hw(fmaf(s0[r], c, nm));
-      const float p1 = exp2_hw(fmaf(s1[r], c, nm));
-      s0[r] = p0;
-      s1[r] = p1;
-      rs += p0 + p1;
-    }
-    l_run += rs;
-
-    // P^T operands: registers 8 hh .. 8 hh + 7 of sub-tile jt hold keys
-    // 32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7.
-    bf16x8 pb[2][2];
+  // P^T operands of a tile, rounded to BF16: registers 8 hh .. 8 hh + 7 of
+  // sub-tile jt hold keys 32 jt + 16 hh + 8 (e/4) + 4 g + e%4, e = 0..7. The
+  // row sum (of the FP32 values) joins l.
+  auto finish_p = [&](const f32x16& p0, const f32x16& p1) {
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {
-      pb[0][hh] = pack_bf16x8(s0[8 * hh + 0], s0[8 * hh + 1], s0[8 * hh + 2], s0[8 * hh + 3],
-                              s0[8 * hh + 4], s0[8 * hh + 5], s0[8 * hh + 6], s0[8 * hh + 7]);
-      pb[1][hh] = pack_bf16x8(s1[8 * hh + 0], s1[8 * hh + 1], s1[8 * hh + 2], s1[8 * hh + 3],
-                              s1[8 * hh + 4], s1[8 * hh + 5], s1[8 * hh + 6], s1[8 * hh + 7]);
+      pb[0][hh] = pack_bf16x8(p0[8 * hh + 0], p0[8 * hh + 1], p0[8 * hh + 2], p0[8 * hh + 3],
+                              p0[8 * hh + 4], p0[8 * hh + 5], p0[8 * hh + 6], p0[8 * hh + 7]);
+      pb[1][hh] = pack_bf16x8(p1[8 * hh + 0], p1[8 * hh + 1], p1[8 * hh + 2], p1[8 * hh + 3],
+                              p1[8 * hh + 4], p1[8 * hh + 5], p1[8 * hh + 6], p1[8 * hh + 7]);
     }
-    // The V^T operand of lane l is column d = 32 dt + l%32 at the same 8 keys,
-    // gathered with two transposed reads of 4 keys each.
-    const char* vb = reinterpret_cast<const char*>(vbuf);
+    float ra = p0[0] + p1[0];
+    float rb = p0[1] + p1[1];
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      ra += p0[r] + p1[r];
+      rb += p0[r + 1] + p1[r + 1];
+    }
+    l_run += ra + rb;
+    // Keep the packing in this step: without this the compiler sinks it into
+    // the next one, past the barrier, where nothing overlaps it.
+    asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l_run));
+  };
+
+  // O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32 at the
+  // same 8 keys as its P^T registers, gathered with two transposed reads of 4 keys.
+  auto pv = [&](const char* vb) {
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
@@ -285,21 +292,104 @@ void fa_fwd_kernel(FwdArgs a) {
       }
   };
 
-  // ---- main loop: the next tile streams into the other buffer during this tile's math.
-  for (int t = 0; t < n_tiles; ++t) {
-    const int kv0 = (t_begin + t) * kFwdKeys;
+  // Row max of a tile (keys kv0 + 32 jt + 8 (r/4) + 4 g + r%4 of row qi): two
+  // chains of three-input maxima, then the other half-wave's value.
+  auto tile_max = [&](const f32x16& s0, const f32x16& s1) {
+    float ma = fmax_ieee(s0[0], s1[0]);
+    float mb = fmax_ieee(s0[1], s1[1]);
+#pragma unroll
+    for (int r = 2; r < 16; r += 2) {
+      ma = fmax_ieee(fmax_ieee(ma, s0[r]), s1[r]);
+      mb = fmax_ieee(fmax_ieee(mb, s0[r + 1]), s1[r + 1]);
+    }
+    return max_xor32(fmax_ieee(ma, mb));
+  };
+
+  // p = 2^(s c - m) in place; with c > 0 a -inf score gives p = 0.
+  auto exps = [&](f32x16& s0, f32x16& s1) {
+    const float nm = m_run == -INFINITY ? 0.f : -m_run;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = exp2_hw(fmaf(s0[r], c, nm));
+      s1[r] = exp2_hw(fmaf(s1[r], c, nm));
+    }
+  };
+
+  // Softmax of tile t (its scores in s0, s1) alongside O += V(t-1)^T P(t-1)
+  // from the V buffer vb: the matrix cores and the vector ALUs of one wave
+  // work at the same time. When a row's reference max moves, l is rescaled at
+  // once and O after P(t-1) V(t-1) has joined it (both were formed at the old
+  // reference). On return pb holds P(t).
+  auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv) {
+    if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
+    const float mt = tile_max(s0, s1) * c;
+    const bool grow = mt > m_run + kRescaleSlack;
+    const bool any_grow = __any(grow);
+    float alpha = 1.f;
+    if (any_grow) {
+      const float m_new = grow ? mt : m_run;
+      alpha = m_new == m_run ? 1.f : exp2_hw(m_run - m_new);  // (also for m = -inf)
+      m_run = m_new;
+      l_run *= alpha;
+    }
+    exps(s0, s1);
+    if (with_pv) {
+      pv(vb);
+      // Each product of P(t-1) with its two V^T reads and a share of this
+      // tile's exponentials.
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+      for (int i = 0; i < 4 * C::DT; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
+      }
+    }
+    finish_p(s0, s1);
+    if (any_grow) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[dt][r] *= alpha;
+    }
+  };
+
+  // One step of the sweep. Step t < n_tiles: the loads of K(t+1) and V(t) are
+  // issued, S(t) = K(t) Q^T is formed, then the softmax of tile t runs with
+  // O += V(t-1)^T P(t-1). Step n_tiles only adds V^T P of the last tile. KB =
+  // t & 1 is a compile-time constant, so every LDS address is a per-lane
+  // register plus an immediate.
+  auto step = [&](auto kb_c, int t, bool with_pv) {
+    constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) {
-      issue_k(t + 1, k_lds[(t + 1) & 1]);
-      issue_v(t + 1, v_lds[(t + 1) & 1]);
-    }
+    if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
+    issue(vg, vdo, true, t, v_lds[KB]);
     __builtin_amdgcn_sched_barrier(0);
-    if (CAUSAL && kv0 > wave_q1) continue;  // every key of the tile is above this wave's rows
     f32x16 s0, s1;
-    scores(k_lds[t & 1], s0, s1);
-    if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
-    softmax_pv(v_lds[t & 1], s0, s1);
+    scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1);
+    softmax_pv((t_begin + t) * kFwdKeys, s0, s1, reinterpret_cast<const char*>(v_lds[KB ^ 1]), with_pv);
+  };
+  auto last = [&](auto kb_c) {
+    constexpr int KB = decltype(kb_c)::value;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    pv(reinterpret_cast<const char*>(v_lds[KB ^ 1]));
+  };
+
+  // ---- the sweep: step 0 has no product to overlap; the steps in between go
+  // two per trip; the last product follows the last step.
+  step(IC<0>{}, 0, false);
+  int t = 1;
+  for (; t + 1 < n_tiles; t += 2) {
+    step(IC<1>{}, t, true);
+    step(IC<0>{}, t + 1, true);
+  }
+  if (t < n_tiles) {
+    step(IC<1>{}, t, true);
+    last(IC<0>{});
+  } else {
+    last(IC<1>{});
   }
 
   // ---- epilogue: O = O / l, lse = (m + log2 l) ln 2. Unsplit: O rounded to
