@@ -216,10 +216,13 @@ void fa_fwd_kernel(FwdArgs a) {
   f32x16 oacc[C::DT];
 #pragma unroll
   for (int dt = 0; dt < C::DT; ++dt) oacc[dt] = f32x16{};
-  bf16x8 pb[2][2];          // P^T of the previous tile (BF16), consumed one step later
+  f32x16 pp0, pp1;          // p of the previous tile (FP32), packed and summed one step later
+  bf16x8 pb[2][2];          // that tile's P^T operands (BF16)
 
-  // S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains interleave.
-  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1) {
+  // S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains
+  // interleave. With valu, the products also carry the packing and summing of
+  // the previous tile's p (issued in the same region).
+  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu) {
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
@@ -229,12 +232,13 @@ void fa_fwd_kernel(FwdArgs a) {
       s0 = mfma32(k0, qf[kk], s0);
       s1 = mfma32(k1, qf[kk], s1);
     }
-    // Reads run three k-steps ahead of the products.
-    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+    // Reads run two k-steps ahead of the products.
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
       __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-      if (kk + 3 < C::KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (kk + 2 < C::KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (valu) __builtin_amdgcn_sched_group_barrier(0x002, 56 / C::KK, 0);
     }
   };
 
@@ -270,9 +274,6 @@ void fa_fwd_kernel(FwdArgs a) {
       rb += p0[r + 1] + p1[r + 1];
     }
     l_run += ra + rb;
-    // Keep the packing in this step: without this the compiler sinks it into
-    // the next one, past the barrier, where nothing overlaps it.
-    asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l_run));
   };
 
   // O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32 at the
@@ -319,7 +320,7 @@ void fa_fwd_kernel(FwdArgs a) {
   // from the V buffer vb: the matrix cores and the vector ALUs of one wave
   // work at the same time. When a row's reference max moves, l is rescaled at
   // once and O after P(t-1) V(t-1) has joined it (both were formed at the old
-  // reference). On return pb holds P(t).
+  // reference). On return pp0, pp1 hold p of tile t.
   auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv) {
     if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
     const float mt = tile_max(s0, s1) * c;
@@ -345,7 +346,11 @@ void fa_fwd_kernel(FwdArgs a) {
         __builtin_amdgcn_sched_group_barrier(0x002, 9, 0);
       }
     }
-    finish_p(s0, s1);
+    // Keep the exponentials in this step: without this the compiler sinks
+    // them into the next one, past the barrier, next to their first use.
+    asm volatile("" : "+v"(s0), "+v"(s1));
+    pp0 = s0;
+    pp1 = s1;
     if (any_grow) {
 #pragma unroll
       for (int dt = 0; dt < C::DT; ++dt)
@@ -366,14 +371,19 @@ void fa_fwd_kernel(FwdArgs a) {
     if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
     issue(vg, vdo, true, t, v_lds[KB]);
     __builtin_amdgcn_sched_barrier(0);
+    if (with_pv) finish_p(pp0, pp1);
     f32x16 s0, s1;
-    scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1);
+    scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1, with_pv);
+    // Keep the packing and summing beside the score products: without this
+    // the compiler sinks them past the mask branch, next to their first use.
+    if (with_pv) asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l_run));
     softmax_pv((t_begin + t) * kFwdKeys, s0, s1, reinterpret_cast<const char*>(v_lds[KB ^ 1]), with_pv);
   };
   auto last = [&](auto kb_c) {
     constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+    finish_p(pp0, pp1);
     pv(reinterpret_cast<const char*>(v_lds[KB ^ 1]));
   };
 
