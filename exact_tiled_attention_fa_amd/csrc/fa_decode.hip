@@ -18,6 +18,7 @@
 //     instruction); Q^T of up to 16 grouped heads is the B operand, kept in
 //     registers. Lane l then holds head l%16 at 4 keys per 16-key tile.
 //   * Online softmax per head in base 2, reduced over the 4 lanes of a head.
+//   * K and V are read once, with non-temporal loads.
 //   * P V on the vector ALUs: V is loaded with fully coalesced 16-byte reads
 //     (one row per 16 lanes at d = 128), each lane keeps FP32 partial outputs
 //     for its 8 columns and every head of the group; the weights p[key][head]
@@ -110,13 +111,13 @@ void fa_decode_split_kernel(DecArgs a) {
       const int key = min(kw + tt * 16 + n, key_end - 1);
       const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)key * D);
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) kf[tt][kk] = __builtin_bit_cast(bf16x8, krow[4 * kk + quad]);
+      for (int kk = 0; kk < C::KK; ++kk) kf[tt][kk] = __builtin_bit_cast(bf16x8, load_nt(krow + 4 * kk + quad));
     }
     uint4 vr[C::NV];
 #pragma unroll
     for (int x = 0; x < C::NV; ++x) {
       const int key = min(kw + rl + C::RPI * x, key_end - 1);
-      vr[x] = *reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)key * D + cl * 8);
+      vr[x] = load_nt(a.v + kv_base + (size_t)key * D + cl * 8);
     }
 
     // ---- S^T tiles: lane holds head n, keys kw + 16 tt + 4 quad + r

@@ -49,6 +49,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // log2(x) (v_log_f32).
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// 16-byte global load with the non-temporal hint: for data read exactly once
+// (a KV cache in decode), so it does not displace reusable lines in the caches.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+
 // IEEE 754-2019 maximum (NaN-propagating). Unlike fmaxf it needs no quieting
 // of its operands, and chains max(max(a, b), c) become one v_maximum3_f32.
 __device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
