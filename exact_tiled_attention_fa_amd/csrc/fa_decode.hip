@@ -41,12 +41,6 @@ struct DecCfg {
   static constexpr int KK = D / 32;          // k-steps of the 16x16x32 MFMA
 };
 
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Up to 4 query heads per group the kernel fits 128 VGPRs: four work-groups
 // per CU, so the workload's 2048 work-groups run in exactly two rounds.
 template <int D, int GM>

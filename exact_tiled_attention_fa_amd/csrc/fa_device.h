@@ -49,6 +49,14 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 // log2(x) (v_log_f32).
 __device__ __forceinline__ float log2_hw(float x) { return __builtin_amdgcn_logf(x); }
 
+// LDS writes of some lanes of a wave made visible to reads by other lanes of
+// the same wave.
+__device__ __forceinline__ void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // 16-byte global load with the non-temporal hint: for data read exactly once
 // (a KV cache in decode), so it does not displace reusable lines in the caches.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
