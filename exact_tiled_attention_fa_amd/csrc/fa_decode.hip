@@ -30,6 +30,69 @@
 
 namespace fa {
 
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
+  return x;
+}
+
+// Log-sum-exp merge of S normalised partial results of one row, by one wave:
+// M = max_s lse_s, w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s,
+// lse = M + ln sum_s w_s. Partial s of the row is o_part[s * D ..]; its lse is
+// lse_part[s]. Lanes load the lse values in parallel; the weights are then
+// broadcast with readlane while each lane accumulates D / 64 columns.
+template <int D>
+__device__ __forceinline__ void combine_row(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                                            int S, uint16_t* __restrict__ o_row, float* __restrict__ lse_out) {
+  constexpr int PER = D / 64;
+  const int lane = __lane_id();
+  float M = -INFINITY;
+  for (int s0 = 0; s0 < S; s0 += 64) M = fmaxf(M, s0 + lane < S ? lse_part[s0 + lane] : -INFINITY);
+  M = wave_max(M);
+  const float Ms = M == -INFINITY ? 0.f : M;
+  float wsum = 0.f;
+  float acc[PER];
+#pragma unroll
+  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+  for (int s0 = 0; s0 < S; s0 += 64) {
+    const int cnt = min(64, S - s0);
+    const float wl = lane < cnt ? exp2_hw((lse_part[s0 + lane] - Ms) * kLog2e) : 0.f;
+    wsum += wl;
+    int s = 0;
+    for (; s + 4 <= cnt; s += 4) {
+      float v[4][PER];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < PER; ++j) v[u][j] = o_part[(size_t)(s0 + s + u) * D + lane * PER + j];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
+#pragma unroll
+        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, v[u][j], acc[j]);
+      }
+    }
+    for (; s < cnt; ++s) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, o_part[(size_t)(s0 + s) * D + lane * PER + j], acc[j]);
+    }
+  }
+  wsum = wave_sum(wsum);
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const __bf16 bv = (__bf16)(acc[j] * inv);
+    o_row[lane * PER + j] = __builtin_bit_cast(uint16_t, bv);
+  }
+  if (lane == 0) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+}
+
 constexpr int kDecWaveKeys = 32;
 constexpr int kDecStepKeys = 4 * kDecWaveKeys;
 

@@ -107,68 +107,62 @@ __device__ __forceinline__ bf16x8 join_bf16x8(i16x4 lo, i16x4 hi) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x = fmaxf(x, shfl_xor(x, m));
-  return x;
-}
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) x += shfl_xor(x, m);
-  return x;
+// Four floats to four BF16 (nearest even), packed little-end first.
+__device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float a3) {
+  __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1, b2 = (__bf16)a2, b3 = (__bf16)a3;
+  uint2 r;
+  r.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
+  r.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
+  return r;
 }
 
-// Log-sum-exp merge of S normalised partial results of one row, by one wave:
-// M = max_s lse_s, w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s,
-// lse = M + ln sum_s w_s. Partial s of the row is o_part[s * D ..]; its lse is
-// lse_part[s]. Lanes load the lse values in parallel; the weights are then
-// broadcast with readlane while each lane accumulates D / 64 columns.
+// Log-sum-exp merge of the S normalised partial results of one row, for the
+// four columns col .. col + 3 a lane owns: M = max_s lse_s,
+// w_s = 2^((lse_s - M) log2 e), O = sum_s w_s O_s / sum_s w_s,
+// lse = M + ln sum_s w_s. op points at column col of partial 0 (partials D
+// floats apart), lp at the row's S lse values; the loads of up to eight
+// partials are in flight together. O goes to o4 (four BF16, nearest even);
+// lse is written when write_lse.
 template <int D>
-__device__ __forceinline__ void combine_row(const float* __restrict__ o_part, const float* __restrict__ lse_part,
-                                            int S, uint16_t* __restrict__ o_row, float* __restrict__ lse_out) {
-  constexpr int PER = D / 64;
-  const int lane = __lane_id();
+__device__ __forceinline__ void merge_splits4(const float* __restrict__ op, const float* __restrict__ lp, int S,
+                                              uint16_t* __restrict__ o4, float* __restrict__ lse_out,
+                                              bool write_lse) {
   float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 64) M = fmaxf(M, s0 + lane < S ? lse_part[s0 + lane] : -INFINITY);
-  M = wave_max(M);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float l[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) l[u] = s0 + u < S ? lp[s0 + u] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, l[u]);
+  }
   const float Ms = M == -INFINITY ? 0.f : M;
   float wsum = 0.f;
-  float acc[PER];
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = 0; s0 < S; s0 += 8) {
+    float4 v[8];
+    float w[8];
 #pragma unroll
-  for (int j = 0; j < PER; ++j) acc[j] = 0.f;
-  for (int s0 = 0; s0 < S; s0 += 64) {
-    const int cnt = min(64, S - s0);
-    const float wl = lane < cnt ? exp2_hw((lse_part[s0 + lane] - Ms) * kLog2e) : 0.f;
-    wsum += wl;
-    int s = 0;
-    for (; s + 4 <= cnt; s += 4) {
-      float v[4][PER];
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int j = 0; j < PER; ++j) v[u][j] = o_part[(size_t)(s0 + s + u) * D + lane * PER + j];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s + u));
-#pragma unroll
-        for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, v[u][j], acc[j]);
-      }
+    for (int u = 0; u < 8; ++u) {
+      const bool in = s0 + u < S;
+      v[u] = in ? *reinterpret_cast<const float4*>(op + (size_t)(s0 + u) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      w[u] = in ? exp2_hw((lp[s0 + u] - Ms) * kLog2e) : 0.f;
     }
-    for (; s < cnt; ++s) {
-      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
 #pragma unroll
-      for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, o_part[(size_t)(s0 + s) * D + lane * PER + j], acc[j]);
+    for (int u = 0; u < 8; ++u) {
+      wsum += w[u];
+      acc.x = fmaf(w[u], v[u].x, acc.x);
+      acc.y = fmaf(w[u], v[u].y, acc.y);
+      acc.z = fmaf(w[u], v[u].z, acc.z);
+      acc.w = fmaf(w[u], v[u].w, acc.w);
     }
   }
-  wsum = wave_sum(wsum);
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) {
-    const __bf16 bv = (__bf16)(acc[j] * inv);
-    o_row[lane * PER + j] = __builtin_bit_cast(uint16_t, bv);
-  }
-  if (lane == 0) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+  *reinterpret_cast<uint2*>(o4) = pack_bf16x4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (write_lse) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
 }
+
+// Threads per work-group of the merge kernels (D / 4 lanes per row).
+constexpr int kMergeThreads = 256;
 
 // Work-group id -> logical id such that each XCD (work-groups are handed to
 // the 8 XCDs round-robin) receives one contiguous range of logical ids.

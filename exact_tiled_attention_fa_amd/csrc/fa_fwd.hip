@@ -60,13 +60,6 @@ __device__ __forceinline__ int kswz(int r) { return D == 128 ? (r & 15) : ((r >>
 template <int D>
 __device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
-__device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float a3) {
-  __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1, b2 = (__bf16)a2, b3 = (__bf16)a3;
-  uint2 r;
-  r.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-  r.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-  return r;
-}
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave
 // fills bytes 16 l .. 16 l + 15 of the 1 KiB block whose LDS address goes in
@@ -472,17 +465,13 @@ void fa_fwd_kernel(FwdArgs a) {
   }
 }
 
-// Merge each row's non-empty key splits with the log-sum-exp combine:
-// M = max_s lse_s, w_s = 2^((lse_s - M) log2 e), O = sum_s w_s O_s / sum_s w_s,
-// lse = M + ln sum_s w_s. D / 4 lanes take one row, four columns each, so every
-// partial row is one coalesced 16-byte-per-lane load; the loads of up to eight
-// splits are in flight together.
-constexpr int kCombineThreads = 256;
-
+// Merge each row's non-empty key splits with the log-sum-exp combine; D / 4
+// lanes take one row, four columns each, so every partial row is one
+// coalesced 16-byte-per-lane load.
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kCombineThreads) void fa_fwd_combine_kernel(FwdArgs a) {
-  constexpr int LPR = D / 4;                    // lanes per row
-  constexpr int RPG = kCombineThreads / LPR;    // rows per work-group
+__global__ __launch_bounds__(kMergeThreads) void fa_fwd_combine_kernel(FwdArgs a) {
+  constexpr int LPR = D / 4;                 // lanes per row
+  constexpr int RPG = kMergeThreads / LPR;   // rows per work-group
   const size_t rows = (size_t)a.B * a.Hq * a.N;
   const size_t row = (size_t)blockIdx.x * RPG + threadIdx.x / LPR;
   if (row >= rows) return;
@@ -492,35 +481,8 @@ __global__ __launch_bounds__(kCombineThreads) void fa_fwd_combine_kernel(FwdArgs
   const int kv_end = CAUSAL ? min(a.N, qb * kFwdRows + kFwdRows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
   const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
-  const float* lp = a.lse_part + row * a.n_splits;
-  const float* op = a.o_part + row * a.n_splits * D + col;
-
-  float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lp[s]);
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float4 v[8];
-    float w[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool in = s0 + u < S;
-      v[u] = in ? *reinterpret_cast<const float4*>(op + (size_t)(s0 + u) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
-      w[u] = in ? exp2_hw((lp[s0 + u] - Ms) * kLog2e) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      wsum += w[u];
-      acc.x = fmaf(w[u], v[u].x, acc.x);
-      acc.y = fmaf(w[u], v[u].y, acc.y);
-      acc.z = fmaf(w[u], v[u].z, acc.z);
-      acc.w = fmaf(w[u], v[u].w, acc.w);
-    }
-  }
-  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  *reinterpret_cast<uint2*>(a.o + row * D + col) = pack_bf16x4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-  if (col == 0) a.lse[row] = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+  merge_splits4<D>(a.o_part + row * a.n_splits * D + col, a.lse_part + row * a.n_splits, S, a.o + row * D + col,
+                   a.lse + row, col == 0);
 }
 
 template <int D, bool CAUSAL>
@@ -537,9 +499,9 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) 
 template <int D, bool CAUSAL>
 static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t per_wg = kCombineThreads / (D / 4);
+  const size_t per_wg = kMergeThreads / (D / 4);
   hipLaunchKernelGGL((fa_fwd_combine_kernel<D, CAUSAL>), dim3((unsigned)((rows + per_wg - 1) / per_wg)),
-                     dim3(kCombineThreads), 0, stream, a);
+                     dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
