@@ -93,27 +93,30 @@ int check_fwd_args(const void* q, const void* k, const void* v, const void* o, c
 int check_fwd_sizes(int B, int Hq, int N, int d) {
   if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return FA_ERR_SHAPE;
   if (elems(B, Hq, N, d) < 0) return FA_ERR_SHAPE;
-  const int64_t nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
+  const int64_t nqb = (N + fa::kFwdWaveRows * 4 - 1) / (fa::kFwdWaveRows * 4);  // the smaller blocks
   if ((int64_t)B * Hq * nqb > INT32_MAX / 4 || (int64_t)B * Hq * N > INT32_MAX) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
 struct FwdPlan {
-  int nqb, n_splits, split_tiles;
+  int rows, nqb, n_splits, split_tiles;
   int64_t nwg;       // work-groups of the forward launch
   size_t ws_bytes;   // partial-result buffer for a split, 0 otherwise
 };
 
-// Key split for grids that would leave CUs idle: aim at two work-groups per
-// CU, never fewer than kMinSplitTiles key tiles per split.
-FwdPlan plan_fwd(int B, int Hq, int N, int d) {
+// Key split for grids that would leave CUs idle: aim at as many work-groups
+// as fit on the CUs at once (one of 8 waves or two of 4 per CU), never fewer
+// than kMinSplitTiles key tiles per split.
+FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal) {
   FwdPlan p;
-  p.nqb = (N + fa::kFwdRows - 1) / fa::kFwdRows;
+  const int waves = fa::fwd_waves(causal, N);
+  p.rows = fa::kFwdWaveRows * waves;
+  p.nqb = (N + p.rows - 1) / p.rows;
   const int64_t base = (int64_t)B * Hq * p.nqb;
   const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
   p.n_splits = 1;
   p.split_tiles = tiles;
-  const int64_t target = 2 * (int64_t)device_cu_count();
+  const int64_t target = (waves == 8 ? 1 : 2) * (int64_t)device_cu_count();
   if (base < target && tiles >= 2 * kMinSplitTiles) {
     const int64_t want = (target + base - 1) / base;
     p.n_splits = (int)(want < tiles / kMinSplitTiles ? want : tiles / kMinSplitTiles);
@@ -138,6 +141,7 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.lse = lse;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N;
   a.c = scale * fa::kLog2eHost;
+  a.rows = p.rows;
   a.nqb = p.nqb;
   a.nwg = (int)p.nwg;
   a.n_splits = p.n_splits;
@@ -153,7 +157,9 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
 
 extern "C" size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d) {
   if (check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
-  return plan_fwd(B, Hq, N, d).ws_bytes;
+  // Enough for either mask (the plan depends on it).
+  const size_t a = plan_fwd(B, Hq, N, d, false).ws_bytes, c = plan_fwd(B, Hq, N, d, true).ws_bytes;
+  return a > c ? a : c;
 }
 
 extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -162,7 +168,7 @@ extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, f
   int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
   if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -177,7 +183,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
   if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.ws_bytes == 0) return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, nullptr, s);
   void* ws = nullptr;

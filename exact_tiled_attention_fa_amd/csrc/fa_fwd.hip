@@ -41,12 +41,13 @@
 
 namespace fa {
 
-template <int D>
+template <int D, int W>
 struct FwdCfg {
   static constexpr int CPR = D / 8;                       // 16-byte chunks per K/V row
   static constexpr int RPB = 64 / CPR;                    // rows per 1 KiB direct-load block
   static constexpr int BLOCKS = kFwdKeys / RPB;           // 1 KiB blocks per K (or V) tile
-  static constexpr int BPW = BLOCKS / 4;                  // blocks per wave per tile
+  static constexpr int BPW = BLOCKS / W;                  // blocks per wave per tile
+  static constexpr int ROWS = kFwdWaveRows * W;           // query rows per work-group
   static constexpr int TILE_CHUNKS = kFwdKeys * CPR;
   static constexpr int KK = D / 16;                       // k-steps of S^T = K Q^T
   static constexpr int DT = D / 32;                       // 32-wide d tiles of O^T
@@ -93,13 +94,14 @@ using IC = std::integral_constant<int, V>;
 // rescaled together when it does move, so O / l and m + log2 l are unchanged.
 constexpr float kRescaleSlack = 8.f;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kFwdThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+template <int D, bool CAUSAL, int W>
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdArgs a) {
-  using C = FwdCfg<D>;
+  using C = FwdCfg<D, W>;
   // K buffers 0, 1 then V buffers 0, 1; after the sweep each wave stages its
   // output rows here for coalesced stores.
-  __shared__ uint4 smem[4][C::TILE_CHUNKS];
+  // (A tile is 128 d bytes, the FP32 staging of one wave's 32 rows as much.)
+  __shared__ uint4 smem[W < 4 ? 4 : W][C::TILE_CHUNKS];
   uint4 (*k_lds)[C::TILE_CHUNKS] = smem;
   uint4 (*v_lds)[C::TILE_CHUNKS] = smem + 2;
 
@@ -123,14 +125,14 @@ void fa_fwd_kernel(FwdArgs a) {
   const int h = bh - b * a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int N = a.N;
-  const int q0 = qb * kFwdRows;
+  const int q0 = qb * C::ROWS;
   const size_t qo_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
   const int t_begin = split * a.split_tiles;
   const uint16_t* kg = a.k + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
   const uint16_t* vg = a.v + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
   const int n_keys = N - t_begin * kFwdKeys;  // keys from the split's first one to the end
 
-  const int kv_end = CAUSAL ? min(N, q0 + kFwdRows) : N;
+  const int kv_end = CAUSAL ? min(N, q0 + C::ROWS) : N;
   const int n_tiles = min((kv_end + kFwdKeys - 1) / kFwdKeys, t_begin + a.split_tiles) - t_begin;
   if (n_tiles <= 0) return;  // this split lies past the block's last visible key
 
@@ -477,23 +479,29 @@ __global__ __launch_bounds__(kMergeThreads) void fa_fwd_combine_kernel(FwdArgs a
   if (row >= rows) return;
   const int col = 4 * (threadIdx.x % LPR);
   const int n = (int)(row % (size_t)a.N);
-  const int qb = n / kFwdRows;
-  const int kv_end = CAUSAL ? min(a.N, qb * kFwdRows + kFwdRows) : a.N;
+  const int qb = n / a.rows;
+  const int kv_end = CAUSAL ? min(a.N, qb * a.rows + a.rows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
   const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
   merge_splits4<D>(a.o_part + row * a.n_splits * D + col, a.lse_part + row * a.n_splits, S, a.o + row * D + col,
                    a.lse + row, col == 0);
 }
 
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, int W>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL>), dim3(a.nwg), dim3(kFwdThreads), 0, stream, a);
+  hipLaunchKernelGGL((fa_fwd_kernel<D, CAUSAL, W>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.rows == kFwdWaveRows * 8)
+    return causal ? launch_fwd_t<D, true, 8>(a, stream) : launch_fwd_t<D, false, 8>(a, stream);
+  return causal ? launch_fwd_t<D, true, 4>(a, stream) : launch_fwd_t<D, false, 4>(a, stream);
+}
+
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
-  if (d == 128) return causal ? launch_fwd_t<128, true>(a, stream) : launch_fwd_t<128, false>(a, stream);
-  return causal ? launch_fwd_t<64, true>(a, stream) : launch_fwd_t<64, false>(a, stream);
+  return d == 128 ? launch_fwd_d<128>(a, causal, stream) : launch_fwd_d<64>(a, causal, stream);
 }
 
 template <int D, bool CAUSAL>

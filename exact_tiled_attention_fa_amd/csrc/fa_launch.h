@@ -23,6 +23,7 @@ struct FwdArgs {
   float* lse;
   int B, Hq, Hkv, N;
   float c;   // scale * log2(e): scores are handled in base 2
+  int rows;  // query rows per block: 32 x waves per work-group
   int nqb;   // query blocks per head
   int nwg;   // total work-groups
   int n_splits;
@@ -30,9 +31,14 @@ struct FwdArgs {
   float* o_part;
   float* lse_part;
 };
-constexpr int kFwdRows = 128;     // query rows per work-group (4 waves x 32)
 constexpr int kFwdKeys = 64;      // keys per K/V tile
-constexpr int kFwdThreads = 256;
+constexpr int kFwdWaveRows = 32;  // query rows per wave
+
+// Waves per forward work-group: 8 (256 rows, one work-group per CU, every K/V
+// tile it loads serves twice the rows) except for causal sweeps shorter than
+// 16K keys, where 4 (128 rows, two work-groups per CU) waste less on the
+// diagonal: every wave of a block takes every tile of the block.
+inline int fwd_waves(bool causal, int N) { return causal && N < 16384 ? 4 : 8; }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // Merge the key-split partials of a split forward into O (BF16) and lse.
