@@ -294,6 +294,18 @@ def main() -> int:
             extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
                           "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
             del q3, k3, v3, o3, l3
+        # Variable-length decode: the decode workload's shape, cache lengths drawn
+        # uniformly from 1..8192 (seeded); bytes = the K/V rows actually read.
+        vlens = np.random.default_rng(dcase.seed).integers(1, dcase.L + 1, size=dcase.B).astype(np.int32)
+        vlens_t = torch.from_numpy(vlens).to(dev)
+        run_vl = fa.prepare_decode(dq, dk, dv, do, dlse, ws, num_splits=dcase.num_splits, scale=dcase.scale,
+                                   seq_lens=vlens_t)
+        settle(run_vl, 0.2)
+        t_vl = per_call_s(run_vl, 20)
+        vl_bytes = 2 * int(vlens.astype(np.int64).sum()) * dcase.Hkv * dcase.d * 2
+        extra["decode_varlen_B16_Hq32_Hkv8_Lmax8192"] = {
+            "us": round(t_vl * 1e6, 2), "hbm_gbs": round(vl_bytes / t_vl / 1e9, 1),
+            "frac_hbm_peak": round(vl_bytes / t_vl / 1e9 / PEAK_HBM_GBS, 4), "mean_len": float(vlens.mean())}
 
     traffic = measured_traffic()
     result = {

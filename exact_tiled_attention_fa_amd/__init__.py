@@ -73,10 +73,23 @@ def decode_workspace_bytes(B: int, Hq: int, L: int, d: int, num_splits: int) -> 
     return int(_lib.lib().fa_decode_workspace_bytes(B, Hq, L, d, num_splits))
 
 
+def _check_lens(seq_lens: torch.Tensor, B: int, device) -> None:
+    if seq_lens.dtype != torch.int32 or seq_lens.shape != (B,) or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous int32 [B] tensor")
+    if seq_lens.device != device:
+        raise ValueError("seq_lens must be on the same GPU as q")
+
+
 def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 16,
            scale: float | None = None, workspace: torch.Tensor | None = None,
-           out: torch.Tensor | None = None, lse: torch.Tensor | None = None):
-    """Split-KV decode. q [B,Hq,1,d], k/v [B,Hkv,L,d] bf16 -> (o [B,Hq,1,d] bf16, lse [B,Hq] fp32)."""
+           out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+           seq_lens: torch.Tensor | None = None):
+    """Split-KV decode. q [B,Hq,1,d], k/v [B,Hkv,L,d] bf16 -> (o [B,Hq,1,d] bf16, lse [B,Hq] fp32).
+
+    With seq_lens (int32 [B] on the GPU), sequence b attends to its first
+    seq_lens[b] keys only (clamped to [0, L]); the rest of its cache rows are
+    never read.
+    """
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_bf16(name, t, 4)
     B, Hq, one, d = q.shape
@@ -94,10 +107,18 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
-    st = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                              B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
-                              workspace.numel() * workspace.element_size(), _stream_handle(q.device))
-    _lib.check(st, "fa_decode")
+    if seq_lens is None:
+        st = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                  B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), _stream_handle(q.device))
+        _lib.check(st, "fa_decode")
+    else:
+        _check_lens(seq_lens, B, q.device)
+        st = _lib.lib().fa_decode_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                         seq_lens.data_ptr(), B, Hq, Hkv, L, d, num_splits, float(scale),
+                                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                         _stream_handle(q.device))
+        _lib.check(st, "fa_decode_varlen")
     return out, lse
 
 
@@ -135,8 +156,10 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
 
 
 def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
-                   workspace: torch.Tensor, num_splits: int = 16, scale: float | None = None):
-    """Like prepare_fwd, for split-KV decode with a caller-owned workspace."""
+                   workspace: torch.Tensor, num_splits: int = 16, scale: float | None = None,
+                   seq_lens: torch.Tensor | None = None):
+    """Like prepare_fwd, for split-KV decode with a caller-owned workspace
+    (and, with seq_lens, per-sequence key counts as in decode)."""
     for name, t in (("q", q), ("k", k), ("v", v), ("out", out)):
         _check_bf16(name, t, 4)
     B, Hq, one, d = q.shape
@@ -147,14 +170,19 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
-    fn = _lib.lib().fa_decode
-    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-            B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
-            workspace.numel() * workspace.element_size())
+    if seq_lens is None:
+        fn, name = _lib.lib().fa_decode, "fa_decode"
+        head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
+    else:
+        _check_lens(seq_lens, B, q.device)
+        fn, name = _lib.lib().fa_decode_varlen, "fa_decode_varlen"
+        head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(), seq_lens.data_ptr())
+    args = head + (B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
+                   workspace.numel() * workspace.element_size())
     device = q.device
 
     def call():
         st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
         if st:
-            _lib.check(st, "fa_decode")
+            _lib.check(st, name)
     return call

@@ -202,9 +202,11 @@ extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num
   return (bytes + 255) & ~(size_t)255;
 }
 
-extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
-                         int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
-                         void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+namespace {
+
+int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse, const int* lens,
+                int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
+                void* workspace, size_t workspace_bytes, fa_stream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
@@ -236,9 +238,28 @@ extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, f
   a.G = G;
   a.n_hg = n_hg;
   a.c = scale * fa::kLog2eHost;
+  a.lens = lens;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   hipError_t e = fa::launch_decode_split(a, d, gm, s);
   if (e != hipSuccess) return FA_ERR_LAUNCH;
   e = fa::launch_combine(a.o_part, a.lse_part, static_cast<uint16_t*>(o), lse, B * Hq, S, d, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
+                         void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  return decode_impl(q, k, v, o, lse, nullptr, B, Hq, Hkv, L, d, num_splits, scale, workspace, workspace_bytes,
+                     stream);
+}
+
+extern "C" int fa_decode_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                const int* seq_lens, int B, int Hq, int Hkv, int L, int d, int num_splits,
+                                float scale, void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  if (!seq_lens) return FA_ERR_NULL;
+  if (!aligned4(seq_lens)) return FA_ERR_ALIGN;
+  return decode_impl(q, k, v, o, lse, seq_lens, B, Hq, Hkv, L, d, num_splits, scale, workspace, workspace_bytes,
+                     stream);
 }

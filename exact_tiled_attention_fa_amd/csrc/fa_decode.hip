@@ -120,13 +120,21 @@ void fa_decode_split_kernel(DecArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
+  // Chunk index slowest: consecutive work-groups (dealt round-robin to the 8
+  // XCDs) take the same chunk of different sequences and heads, so every XCD
+  // gets an even share of each chunk index, also when per-sequence lengths
+  // leave the later chunks empty.
   int rest = blockIdx.x;
-  const int split = rest % a.S; rest /= a.S;
   const int hg = rest % a.n_hg; rest /= a.n_hg;
-  const int hk = rest % a.Hkv;
-  const int b = rest / a.Hkv;
-  const int key_begin = split * a.chunk;
-  const int key_end = min(a.L, key_begin + a.chunk);
+  const int hk = rest % a.Hkv; rest /= a.Hkv;
+  const int b = rest % a.B;
+  const int split = rest / a.B;
+  // Keys of this sequence and its chunk: with per-sequence lengths the S
+  // chunks cut each sequence's own keys, so the work follows the lengths.
+  const int len = a.lens ? min(max(a.lens[b], 0), a.L) : a.L;
+  const int chunk = a.lens ? (len + a.S - 1) / a.S : a.chunk;
+  const int key_begin = split * chunk;
+  const int key_end = min(len, key_begin + chunk);  // an empty chunk writes O_c = 0, lse_c = -inf
   const int h_first = hk * a.G + hg * GM;
   const int gv = min(GM, a.G - hg * GM);  // valid heads in this work-group
   const float c = a.c;

@@ -57,6 +57,7 @@ struct DecArgs {
   int G;            // query heads per KV head
   int n_hg;         // head groups per KV head (heads per group <= 16)
   float c;          // scale * log2(e)
+  const int* lens;  // per-sequence key counts (clamped to [0, L]), or null: all L
 };
 constexpr int kDecThreads = 256;
 

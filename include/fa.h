@@ -130,6 +130,25 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
               void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
+/*
+ * fa_decode_varlen -- fa_decode over a padded KV cache whose sequences have
+ * their own lengths (a batch of real KV caches). Sequence b attends to keys
+ * 0 .. len_b - 1 of its cache rows, len_b = seq_lens[b] clamped to [0, L];
+ * keys past len_b are never read (they may hold anything). A sequence with
+ * len_b = 0 gets O = 0 and lse = -inf.
+ *
+ *   seq_lens [B] int32, device memory, 4-byte aligned; read by the kernels,
+ *            so it cannot be validated on the host.
+ *   Every other argument, the layouts and the workspace
+ *   (fa_decode_workspace_bytes(B, Hq, L, d, num_splits)) are those of
+ *   fa_decode. Each sequence's own len_b keys are cut into the S chunks that
+ *   fa_decode would use for L (ceil(len_b / S) keys each), so the work of a
+ *   sequence spreads over all of its work-groups.
+ */
+int fa_decode_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* seq_lens,
+                     int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
+                     void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);
 

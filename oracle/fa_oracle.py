@@ -143,6 +143,30 @@ def decode_ref(q, k, v, scale: float):
     return o_out, lse_out
 
 
+def decode_varlen_ref(q, k, v, lens, scale: float):
+    """decode_ref for a batch of KV caches of their own lengths.
+
+    Sequence b attends to keys 0 .. len_b - 1 of its (padded) cache rows, with
+    len_b = lens[b] clamped to [0, L]; the padding takes no part. A sequence
+    with no key has an empty sum: O = 0 and lse = ln 0 = -inf (the defined
+    output for a row with every key masked).
+    """
+    q = np.asarray(q)
+    if q.ndim == 4:
+        q = q[:, :, 0, :]
+    B, Hq, _ = q.shape
+    L = np.asarray(k).shape[2]
+    o_out = np.zeros((B, Hq, np.asarray(v).shape[-1]))
+    lse_out = np.full((B, Hq), -np.inf)
+    for b in range(B):
+        n = int(min(max(int(lens[b]), 0), L))
+        if n == 0:
+            continue
+        o, lse = decode_ref(q[b:b + 1], np.asarray(k)[b:b + 1, :, :n], np.asarray(v)[b:b + 1, :, :n], scale)
+        o_out[b], lse_out[b] = o[0], lse[0]
+    return o_out, lse_out
+
+
 def split_chunks(L: int, num_splits: int):
     """Key ranges of a split-KV decode: chunk = ceil(L / num_splits) keys each."""
     chunk = -(-L // num_splits)

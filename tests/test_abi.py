@@ -26,8 +26,8 @@ def lib():
 
 
 def test_header_declares_the_abi():
-    assert _declared_functions() == ["fa_decode", "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_workspace_bytes",
-                                     "fa_fwd_ws", "fa_status_string"]
+    assert _declared_functions() == ["fa_decode", "fa_decode_varlen", "fa_decode_workspace_bytes", "fa_fwd",
+                                     "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -98,6 +98,21 @@ def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4
 ])
 def test_decode_rejects(lib, kw, status):
     assert dec(lib, **kw) == status
+
+
+def dec_varlen(lib, lens=P, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4, scale=0.1, ws=P, wsb=1 << 30)
+    a.update(kw)
+    return lib.fa_decode_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], lens, a["B"], a["Hq"], a["Hkv"], a["L"],
+                                a["d"], a["splits"], a["scale"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(lens=None), -1), (dict(lens=P + 2), -5), (dict(q=None), -1), (dict(L=0), -2), (dict(d=80), -3),
+    (dict(Hq=6, Hkv=4), -4), (dict(v=BAD), -5), (dict(scale=float("nan")), -8), (dict(wsb=16), -6),
+])
+def test_decode_varlen_rejects(lib, kw, status):
+    assert dec_varlen(lib, **kw) == status
 
 
 def test_decode_workspace_size(lib):

@@ -255,6 +255,40 @@ def test_decode_is_last_causal_row():
     assert np.max(np.abs(lsed - lse[:, :, N - 1])) < 1e-14
 
 
+def test_decode_varlen_is_causal_row_at_its_length():
+    """Sequence b with len_b keys equals row len_b - 1 of causal attention over its
+    padded cache: the causal mask, not slicing, limits the keys there. Padding
+    holding NaN and huge values takes no part."""
+    rng = np.random.default_rng(14)
+    B, Hq, Hkv, L, d = 4, 4, 2, 40, 8
+    q, k, v = _rand(rng, B, Hq, 1, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    lens = np.array([1, 17, 39, 40])
+    kp, vp = k.copy(), v.copy()
+    for b, n in enumerate(lens):
+        kp[b, :, n:] = np.nan
+        vp[b, :, n:] = 1e30
+    od, ld = fa_oracle.decode_varlen_ref(q, kp, vp, lens, 0.3)
+    assert np.isfinite(od).all() and np.isfinite(ld).all()
+    for b, n in enumerate(lens):
+        qc = np.repeat(q[b:b + 1], L, axis=2)  # the query at every row; row n - 1 is the one that counts
+        o, lse = fa_oracle.attention_ref(qc, k[b:b + 1], v[b:b + 1], True, 0.3, rows=np.full((Hq, 1), n - 1))
+        assert np.max(np.abs(od[b] - o[0, :, 0])) < 1e-14
+        assert np.max(np.abs(ld[b] - lse[0, :, 0])) < 1e-14
+
+
+def test_decode_varlen_closed_forms():
+    rng = np.random.default_rng(15)
+    B, Hq, Hkv, L, d = 4, 4, 2, 9, 8
+    q, k, v = _rand(rng, B, Hq, 1, d), _rand(rng, B, Hkv, L, d), _rand(rng, B, Hkv, L, d)
+    od, ld = fa_oracle.decode_varlen_ref(q, k, v, [1, 0, -3, 99], 0.5)
+    for h in range(Hq):  # one key: O = v_0, lse = scale q.k_0
+        assert np.allclose(od[0, h], v[0, h // 2, 0], atol=0, rtol=1e-15)
+        assert math.isclose(ld[0, h], 0.5 * float(np.dot(q[0, h, 0], k[0, h // 2, 0])), rel_tol=1e-14)
+    assert (od[1:3] == 0).all() and np.isneginf(ld[1:3]).all()  # no key (a negative count means none)
+    of, lf = fa_oracle.decode_ref(q[3:], k[3:], v[3:], 0.5)  # a count past L means all L keys
+    assert np.max(np.abs(od[3] - of[0])) < 1e-15 and np.max(np.abs(ld[3] - lf[0])) < 1e-15
+
+
 def test_sampled_rows_equal_full_rows():
     rng = np.random.default_rng(12)
     N = 300
@@ -315,6 +349,11 @@ def _pins_hold_inner(mod):
     ok &= bool(np.max(np.abs(od - oc)) < 1e-12 and np.max(np.abs(ld - lc)) < 1e-12)
     ob, lb = _brute(qd[0].tolist(), kd[0].tolist(), vd[0].tolist(), False, 0.5)
     ok &= bool(np.max(np.abs(od[0] - ob[:, 0])) < 1e-12)
+    # variable-length decode: brute force over the first n keys
+    for n in (1, 7, 20):
+        ov, lv = mod.decode_varlen_ref(qd, kd, vd, [n], 0.5)
+        ob, lb = _brute(qd[0].tolist(), kd[0, :, :n].tolist(), vd[0, :, :n].tolist(), False, 0.5)
+        ok &= bool(np.max(np.abs(ov[0] - ob[:, 0])) < 1e-12 and np.max(np.abs(lv[0] - lb[:, 0])) < 1e-12)
     return ok
 
 
@@ -370,3 +409,12 @@ def test_pins_catch_planted_mistakes(monkeypatch):
 
     monkeypatch.setattr(fa_oracle, "attention_ref", wrong_group)
     assert not _pins_hold(fa_oracle)
+    monkeypatch.setattr(fa_oracle, "attention_ref", orig_attn)
+
+    # A variable-length decode that takes one key too many, or ignores the lengths.
+    orig_varlen = fa_oracle.decode_varlen_ref
+    for bad_lens in (lambda lens: [n + 1 for n in lens], lambda lens: [10 ** 9 for _ in lens]):
+        monkeypatch.setattr(fa_oracle, "decode_varlen_ref",
+                            lambda q, k, v, lens, scale, f=bad_lens: orig_varlen(q, k, v, f(lens), scale))
+        assert not _pins_hold(fa_oracle)
+    monkeypatch.setattr(fa_oracle, "decode_varlen_ref", orig_varlen)
