@@ -117,6 +117,68 @@ def attention_ref(q, k, v, causal: bool, scale: float, rows=None, return_p: bool
     return o_out, lse_out
 
 
+def attention_bwd_ref(q, k, v, do, causal: bool, scale: float, rows=None, key_rows=None):
+    """Gradients of the exact attention of attention_ref, contracted with dO.
+
+    "Why is standard attention memory-bound, and how does FlashAttention fix
+    it?" ("Step 4: The result is exact, and the backward pass recomputes"; FAQ
+    "Why does the backward pass recompute the scores?"): the backward pass
+    needs the scores, which FlashAttention recomputes tile by tile from Q, K and
+    the saved per-row statistics. The pages state no formulas; this is the
+    plain chain rule through O = P V, P = softmax(S), S = scale Q K^T, with S,
+    P, dP and dS materialised (row chunks of all query rows):
+
+        dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+        dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+
+    GQA: the gradients of a KV head sum over the query heads that read it.
+    q, do: [B, Hq, N, d]; k, v: [B, Hkv, N, d]. rows / key_rows select the
+    query rows of dQ and the key rows of dK, dV (None: all; 1-D: the same for
+    every head; 2-D: per query head / per KV head). Returns dQ [B, Hq, R, d],
+    dK [B, Hkv, Rk, d], dV [B, Hkv, Rk, dv] in float64.
+    """
+    q, k, v, do = (np.asarray(x) for x in (q, k, v, do))
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if Hq % Hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    group = Hq // Hkv
+    R = len(_rows_for_head(rows, 0, N))
+    Rk = len(_rows_for_head(key_rows, 0, N))
+    dvw = v.shape[-1]
+    dq_out = np.zeros((B, Hq, R, d))
+    dk_out = np.zeros((B, Hkv, Rk, d))
+    dv_out = np.zeros((B, Hkv, Rk, dvw))
+    for b in range(B):
+        for h in range(Hq):
+            g = h // group
+            kh, vh = _as_f64(k[b, g]), _as_f64(v[b, g])
+            rid = _rows_for_head(rows, h, N)
+            kid = _rows_for_head(key_rows, g, N)
+            where = {int(r): n for n, r in enumerate(rid)}
+            for c0 in range(0, N, ROW_CHUNK):
+                ids = np.arange(c0, min(N, c0 + ROW_CHUNK))
+                qr, dor = _as_f64(q[b, h, ids]), _as_f64(do[b, h, ids])
+                _, _, p = _standard_attention_rows(qr, kh, vh, scale, ids, causal)
+                dp = dor @ vh.T
+                dsum = (p * dp).sum(axis=1)
+                ds = p * (dp - dsum[:, None])
+                dv_out[b, g] += p[:, kid].T @ dor
+                dk_out[b, g] += scale * (ds[:, kid].T @ qr)
+                for n_local, r in enumerate(ids):
+                    if int(r) in where:
+                        dq_out[b, h, where[int(r)]] = scale * (ds[n_local] @ kh)
+    return dq_out, dk_out, dv_out
+
+
+def bwd_flops(N: int, d: int, causal: bool, heads: int = 1) -> float:
+    """Algorithmic backward FLOPs: five N x N x d products (S, dV, dP, dQ, dK),
+    10 N^2 d per head, halved for causal (the usual count; recomputation of S
+    is included, extra recomputation by an implementation is not)."""
+    f = 10.0 * N * N * d * heads
+    return f / 2 if causal else f
+
+
 def decode_ref(q, k, v, scale: float):
     """One query token per (sequence, query head) against the whole KV cache.
 
