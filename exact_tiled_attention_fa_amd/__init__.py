@@ -16,7 +16,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "decode", "fwd_workspace_bytes", "decode_workspace_bytes", "prepare_fwd", "prepare_decode",
+__all__ = ["fwd", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes", "bwd_workspace_bytes",
+           "prepare_fwd", "prepare_decode", "prepare_bwd",
            "FaError"]
 
 
@@ -120,6 +121,56 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 
                                          _stream_handle(q.device))
         _lib.check(st, "fa_decode_varlen")
     return out, lse
+
+
+def bwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
+    return int(_lib.lib().fa_bwd_workspace_bytes(B, Hq, N, d))
+
+
+def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace):
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dout", dout), ("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bf16(name, t, 4)
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape or dk.shape != k.shape or dv.shape != k.shape:
+        raise ValueError("k, v, dk, dv must be [B,Hkv,N,d]")
+    if o.shape != q.shape or dout.shape != q.shape or dq.shape != q.shape:
+        raise ValueError("o, dout, dq must be [B,Hq,N,d]")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
+            dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv, N, d, int(bool(causal)), float(scale),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size())
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
+        dout: torch.Tensor, causal: bool = False, scale: float | None = None,
+        workspace: torch.Tensor | None = None):
+    """Backward pass of fwd (d = 128): (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]) bf16, from the
+    forward's o and lse and the upstream gradient dout."""
+    B, Hq, N, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(bwd_workspace_bytes(B, Hq, N, d), 16), dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    st = _lib.lib().fa_bwd(*_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace),
+                           _stream_handle(q.device))
+    _lib.check(st, "fa_bwd")
+    return dq, dk, dv
+
+
+def prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = False, scale: float | None = None):
+    """Like prepare_fwd, for the backward pass with caller-owned outputs and workspace."""
+    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace)
+    fn = _lib.lib().fa_bwd
+    device = q.device
+
+    def call():
+        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        if st:
+            _lib.check(st, "fa_bwd")
+    return call
 
 
 def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,

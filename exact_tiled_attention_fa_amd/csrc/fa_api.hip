@@ -193,6 +193,58 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
 }
 
+namespace {
+
+int64_t bwd_npad(int N) { return ((int64_t)N + fa::kBwdTile - 1) / fa::kBwdTile * fa::kBwdTile; }
+
+}  // namespace
+
+extern "C" size_t fa_bwd_workspace_bytes(int B, int Hq, int N, int d) {
+  if (d != 128 || check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
+  const size_t bytes = (size_t)2 * B * Hq * (size_t)bwd_npad(N) * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                      const void* dout, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d,
+                      int causal, float scale, void* workspace, size_t workspace_bytes, fa_stream_t stream) {
+  if (!o || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+  int st = check_fwd_args(q, k, v, dq, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_HEAD_DIM;
+  if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
+  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
+  const size_t need = fa_bwd_workspace_bytes(B, Hq, N, d);
+  if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  const int64_t npad = bwd_npad(N);
+  const int64_t nkb = (N + fa::kBwdKeyBlock - 1) / fa::kBwdKeyBlock;
+  const int64_t nqb = (N + fa::kBwdRowBlock - 1) / fa::kBwdRowBlock;
+  if ((int64_t)B * Hkv * nkb > INT32_MAX || (int64_t)B * Hq * nqb > INT32_MAX ||
+      (int64_t)B * Hq * npad / 16 > INT32_MAX)
+    return FA_ERR_SHAPE;
+
+  fa::BwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<const uint16_t*>(o);
+  a.dout = static_cast<const uint16_t*>(dout);
+  a.lse = lse;
+  a.dq = static_cast<uint16_t*>(dq);
+  a.dk = static_cast<uint16_t*>(dk);
+  a.dv = static_cast<uint16_t*>(dv);
+  a.lse2 = static_cast<float*>(workspace);
+  a.delta = a.lse2 + (size_t)B * Hq * npad;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.Npad = (int)npad;
+  a.c = scale * fa::kLog2eHost;
+  a.scale = scale;
+  a.nkb = (int)nkb;
+  a.nqb = (int)nqb;
+  const hipError_t e = fa::launch_bwd(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
 extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits) {
   if (B <= 0 || Hq <= 0 || L <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > L) return 0;
   const int S = decode_splits_used(L, num_splits);

@@ -1,0 +1,426 @@
+// Backward pass of exact attention for gfx950 (head dim 128).
+//
+// What it computes: with P = softmax(scale Q K^T) (masked when causal) and the
+// upstream gradient dO, the chain rule through O = P V gives
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - delta),  delta_i = sum_t dO_it O_it,
+//   dQ = scale dS K,  dK = scale dS^T Q,
+// and for GQA a KV head's dK, dV sum over the query heads that read it. As the
+// pages describe for training ("Why is standard attention memory-bound, and
+// how does FlashAttention fix it?", "Step 4: The result is exact, and the
+// backward pass recomputes"), the scores are recomputed tile by tile from Q, K
+// and the per-row statistic lse the forward pass saved; no N x N matrix is
+// stored.
+//
+// Three launches:
+//   * row pass: lse2 = lse log2(e) and delta = rowsum(dO O) per query row
+//     (the forward's O; sum_j P_ij dP_ij = sum_t dO_it O_it);
+//   * dK/dV: one work-group of 4 waves per (batch, KV head, 64-key block);
+//     each wave owns 16 keys and keeps K^T and V^T of them in registers as
+//     v_mfma_f32_16x16x32_bf16 B operands. It sweeps 64-row tiles of Q and dO
+//     (double-buffered in LDS by direct loads) of every query head of the
+//     group: S = Q K^T and dP = dO V^T (lane = key, four query rows per
+//     register group), P = 2^(S c - lse2), dS = P (dP - delta), then
+//     dV += P^T dO and dK += dS^T Q with the P / dS registers as A operands
+//     and dO / Q gathered by transposed LDS reads;
+//   * dQ: one work-group of 4 waves per (batch, query head, 128-row block),
+//     the forward's layout: S^T = K Q^T and dP^T = V dO^T (lane = query row),
+//     dS^T packed to BF16 as the B operand of dQ^T += K^T dS^T with K^T
+//     gathered by transposed reads.
+// Tiles that hold both row reads and transposed reads use a swizzle that keeps
+// both patterns free of bank conflicts (sw2 below).
+#include "fa_device.h"
+#include "fa_launch.h"
+
+namespace fa {
+
+namespace {
+
+constexpr int kD = 128;
+constexpr int kCPR = kD / 8;                 // 16-byte chunks per row
+constexpr int kTileChunks = kBwdTile * kCPR;  // 16 KiB tiles
+constexpr int kKK32 = kD / 16;               // k-steps of a 32x32x16 product over d
+constexpr int kDT = kD / 32;                 // 32-wide d tiles
+constexpr int kKK16 = kD / 32;               // k-steps of a 16x16x32 product over d
+constexpr int kTT = kD / 16;                 // 16-wide d tiles
+
+// XOR swizzle of the 16-byte chunk index of tile row r. Bijective on r & 15,
+// so 16 consecutive rows read at one chunk hit 16 different bank groups; and
+// for the transposed reads (4 consecutive rows from a 4-aligned start, two
+// adjacent chunks) it takes 8 different values. Rows 16 apart share it.
+__device__ __forceinline__ int sw2(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// Swizzle of tiles read by rows only (as the forward's K tiles).
+__device__ __forceinline__ int swr(int r) { return r & 15; }
+
+// Direct loads of a 64-row tile of a row-major [rows, 128] BF16 matrix into
+// LDS: wave w fills the 1 KiB blocks 4 w .. 4 w + 3 (4 rows each); lane l
+// writes physical chunk l % 16 of its row with logical chunk (l % 16) ^ sw.
+// Rows past `rows` read the last row (finite data the caller masks).
+template <bool SW2>
+__device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int rows, uint4* dst, int wave, int lane) {
+  const int pc = lane & 15;
+  const uint32_t l0 = lds_addr(dst) + 4096u * (uint32_t)wave;
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int r = 16 * wave + 4 * x + (lane >> 4);
+    const int sw = SW2 ? sw2(r) : swr(r);
+    const int row = min(row0 + r, rows - 1);
+    dma16(src, 2u * (uint32_t)(row * kD + 8 * (pc ^ sw)), l0 + 1024u * x);
+  }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- row pass
+// 16 lanes per row (8 columns each): delta = sum_t dO O in FP32, lse2 = lse
+// log2(e); rows N .. Npad - 1 of each head get zeros.
+__global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
+  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int c16 = threadIdx.x & 15;
+  const size_t rows = (size_t)a.B * a.Hq * a.Npad;
+  if (row >= rows) return;
+  const size_t bh = row / a.Npad;
+  const int n = (int)(row - bh * a.Npad);
+  float s = 0.f;
+  if (n < a.N) {
+    const size_t src = (bh * a.N + n) * kD + 8 * c16;
+    const uint4 x = *reinterpret_cast<const uint4*>(a.o + src);
+    const uint4 y = *reinterpret_cast<const uint4*>(a.dout + src);
+    s = bf16_lo(x.x) * bf16_lo(y.x) + bf16_hi(x.x) * bf16_hi(y.x) + bf16_lo(x.y) * bf16_lo(y.y) +
+        bf16_hi(x.y) * bf16_hi(y.y) + bf16_lo(x.z) * bf16_lo(y.z) + bf16_hi(x.z) * bf16_hi(y.z) +
+        bf16_lo(x.w) * bf16_lo(y.w) + bf16_hi(x.w) * bf16_hi(y.w);
+  }
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) s += shfl_xor(s, m);
+  if (c16 == 0) {
+    a.delta[row] = s;
+    a.lse2[row] = n < a.N ? a.lse[bh * a.N + n] * kLog2e : 0.f;
+  }
+}
+
+// ---------------------------------------------------------------- dK, dV
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
+  __shared__ uint4 q_lds[2][kTileChunks];
+  __shared__ uint4 do_lds[2][kTileChunks];
+  __shared__ float4 st_lds[2][2][kBwdTile / 4];  // [buffer][lse2 | delta][rows / 4]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b16 = lane >> 4;  // 16-lane block
+  const int j16 = lane & 15;
+
+  // Grid: XCD-contiguous; KV heads outermost, then key blocks (the first key
+  // blocks have the most query tiles when causal, so they start first).
+  const int lid = xcd_contiguous(blockIdx.x, nwg);
+  const int bhk = lid / a.nkb;
+  const int kb = lid - bhk * a.nkb;
+  const int b = bhk / a.Hkv;
+  const int hk = bhk - b * a.Hkv;
+  const int G = a.Hq / a.Hkv;
+  const int N = a.N;
+  const int j0 = kb * kBwdKeyBlock;
+  const int key = j0 + 16 * wave + j16;  // this lane's key (S columns, P^T rows)
+  const size_t kv_base = (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
+
+  // K^T and V^T as B operands: lane holds row `key`, columns 32 kk + 8 b16 .. + 7.
+  bf16x8 kf[kKK16], vf[kKK16];
+  {
+    const int kr = min(key, N - 1);
+    const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)kr * kD);
+    const uint4* vrow = reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)kr * kD);
+#pragma unroll
+    for (int kk = 0; kk < kKK16; ++kk) {
+      kf[kk] = __builtin_bit_cast(bf16x8, krow[4 * kk + b16]);
+      vf[kk] = __builtin_bit_cast(bf16x8, vrow[4 * kk + b16]);
+    }
+  }
+
+  // Query tiles: for each query head of the group, tiles u_begin .. n_u - 1
+  // (causal: none above the key block).
+  const int n_u = (N + kBwdTile - 1) / kBwdTile;
+  const int u_begin = CAUSAL ? j0 / kBwdTile : 0;
+  const int per_head = n_u - u_begin;
+  const int n_t = G * per_head;
+
+  auto issue = [&](int t, int buf) {
+    const int hq = hk * G + t / per_head;
+    const int u = u_begin + t % per_head;
+    const size_t rb = (size_t)(b * a.Hq + hq);
+    load_tile<true>(a.q + rb * N * kD, u * kBwdTile, N, q_lds[buf], wave, lane);
+    load_tile<true>(a.dout + rb * N * kD, u * kBwdTile, N, do_lds[buf], wave, lane);
+    if (wave == 0 && lane < 16) {  // lse2 and delta of the tile's 64 rows (256 B each)
+      const size_t off = rb * a.Npad + (size_t)u * kBwdTile;
+      dma16(a.lse2 + off, 16u * (uint32_t)lane, lds_addr(&st_lds[buf][0][0]));
+      dma16(a.delta + off, 16u * (uint32_t)lane, lds_addr(&st_lds[buf][1][0]));
+    }
+  };
+
+  // Per-lane LDS byte offsets. A fragments (rows): row 16 qt + j16, chunk 4 kk + b16.
+  int aoff[kKK16];
+#pragma unroll
+  for (int kk = 0; kk < kKK16; ++kk) aoff[kk] = 16 * (j16 * kCPR + ((4 * kk + b16) ^ sw2(j16)));
+  // Transposed reads: lane names row 4 b16 + j16 / 4 (+ 32 u2, + 16 for the
+  // second half) and 4 columns at 16 tt + 4 (j16 % 4); lane l receives column
+  // 16 tt + j16 of rows 4 b16 .. 4 b16 + 3.
+  int troff[kTT];
+  {
+    const int r0 = 4 * b16 + (j16 >> 2);
+#pragma unroll
+    for (int tt = 0; tt < kTT; ++tt)
+      troff[tt] = 16 * (r0 * kCPR + ((2 * tt + ((j16 & 3) >> 1)) ^ sw2(r0))) + 8 * (j16 & 1);
+  }
+
+  f32x4 dk[kTT], dv[kTT];
+#pragma unroll
+  for (int tt = 0; tt < kTT; ++tt) dk[tt] = dv[tt] = f32x4{};
+
+  const float c = a.c;
+  issue(0, 0);  // n_t >= 1: the key block lies below N
+  for (int t = 0; t < n_t; ++t) {
+    const int buf = t & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < n_t) issue(t + 1, buf ^ 1);
+    const int u = u_begin + t % per_head;
+    const int i0 = u * kBwdTile;
+    const char* qb = reinterpret_cast<const char*>(q_lds[buf]);
+    const char* db = reinterpret_cast<const char*>(do_lds[buf]);
+
+    // S = Q K^T and dP = dO V^T for 4 groups of 16 query rows.
+    f32x4 s[4], dp[4];
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      s[qt] = f32x4{};
+      dp[qt] = f32x4{};
+#pragma unroll
+      for (int kk = 0; kk < kKK16; ++kk) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * kCPR * 16);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * kCPR * 16);
+        s[qt] = mfma16(qa, kf[kk], s[qt]);
+        dp[qt] = mfma16(da, vf[kk], dp[qt]);
+      }
+    }
+    // P and dS: lane holds key `key`, query rows i0 + 16 qt + 4 b16 + r.
+#pragma unroll
+    for (int qt = 0; qt < 4; ++qt) {
+      const float4 l4 = st_lds[buf][0][4 * qt + b16];
+      const float4 d4 = st_lds[buf][1][4 * qt + b16];
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int qrow = i0 + 16 * qt + 4 * b16 + r;
+        const bool vis = qrow < N && key < N && (!CAUSAL || key <= qrow);
+        const float p = vis ? exp2_hw(fmaf(s[qt][r], c, -lv[r])) : 0.f;
+        s[qt][r] = p;
+        dp[qt][r] = p * (dp[qt][r] - dl[r]);
+      }
+    }
+    // dV += P^T dO and dK += dS^T Q over two 32-row halves: the A operand of
+    // half u2 is rows 32 u2 + 4 b16 + (0..3) and 32 u2 + 16 + 4 b16 + (0..3).
+#pragma unroll
+    for (int u2 = 0; u2 < 2; ++u2) {
+      const bf16x8 pa = pack_bf16x8(s[2 * u2][0], s[2 * u2][1], s[2 * u2][2], s[2 * u2][3],
+                                    s[2 * u2 + 1][0], s[2 * u2 + 1][1], s[2 * u2 + 1][2], s[2 * u2 + 1][3]);
+      const bf16x8 sa = pack_bf16x8(dp[2 * u2][0], dp[2 * u2][1], dp[2 * u2][2], dp[2 * u2][3],
+                                    dp[2 * u2 + 1][0], dp[2 * u2 + 1][1], dp[2 * u2 + 1][2], dp[2 * u2 + 1][3]);
+      const int ro = u2 * 32 * kCPR * 16;
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        const i16x4 dlo = lds_read_tr(db + troff[tt] + ro);
+        const i16x4 dhi = lds_read_tr(db + troff[tt] + ro + 16 * kCPR * 16);
+        dv[tt] = mfma16(pa, join_bf16x8(dlo, dhi), dv[tt]);
+        const i16x4 qlo = lds_read_tr(qb + troff[tt] + ro);
+        const i16x4 qhi = lds_read_tr(qb + troff[tt] + ro + 16 * kCPR * 16);
+        dk[tt] = mfma16(sa, join_bf16x8(qlo, qhi), dk[tt]);
+      }
+    }
+  }
+
+  // Epilogue: lane holds keys j0 + 16 wave + 4 b16 + r, column 16 tt + j16.
+  const float sc = a.scale;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int kr = j0 + 16 * wave + 4 * b16 + r;
+    if (kr < N) {
+      uint16_t* dkrow = a.dk + kv_base + (size_t)kr * kD;
+      uint16_t* dvrow = a.dv + kv_base + (size_t)kr * kD;
+#pragma unroll
+      for (int tt = 0; tt < kTT; ++tt) {
+        dkrow[16 * tt + j16] = __builtin_bit_cast(uint16_t, (__bf16)(dk[tt][r] * sc));
+        dvrow[16 * tt + j16] = __builtin_bit_cast(uint16_t, (__bf16)dv[tt][r]);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- dQ
+template <bool CAUSAL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
+  __shared__ uint4 k_lds[2][kTileChunks];
+  __shared__ uint4 v_lds[2][kTileChunks];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 5;
+  const int li = lane & 31;
+
+  const int lid = xcd_contiguous(blockIdx.x, nwg);
+  const int bh = lid / a.nqb;
+  int qb = lid - bh * a.nqb;
+  if (CAUSAL) qb = a.nqb - 1 - qb;  // heaviest first
+  const int b = bh / a.Hq;
+  const int h = bh - b * a.Hq;
+  const int hk = h / (a.Hq / a.Hkv);
+  const int N = a.N;
+  const int q0 = qb * kBwdRowBlock;
+  const int qi = q0 + 32 * wave + li;
+  const size_t q_base = (size_t)(b * a.Hq + h) * (size_t)N * kD;
+  const uint16_t* kg = a.k + (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
+  const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
+  const int kv_end = CAUSAL ? min(N, q0 + kBwdRowBlock) : N;
+  const int n_tiles = (kv_end + kBwdTile - 1) / kBwdTile;
+
+  load_tile<true>(kg, 0, N, k_lds[0], wave, lane);
+  load_tile<false>(vg, 0, N, v_lds[0], wave, lane);
+
+  // Q^T and dO^T as B operands (lane = query row qi), lse2 and delta of qi.
+  bf16x8 qf[kKK32], df[kKK32];
+  {
+    const size_t r = q_base + (size_t)(qi < N ? qi : 0) * kD;
+    const uint4* qrow = reinterpret_cast<const uint4*>(a.q + r);
+    const uint4* drow = reinterpret_cast<const uint4*>(a.dout + r);
+#pragma unroll
+    for (int kk = 0; kk < kKK32; ++kk) {
+      qf[kk] = __builtin_bit_cast(bf16x8, qrow[2 * kk + g]);
+      df[kk] = __builtin_bit_cast(bf16x8, drow[2 * kk + g]);
+    }
+  }
+  const size_t st = (size_t)(b * a.Hq + h) * a.Npad + (qi < N ? qi : 0);
+  const float lse2 = a.lse2[st];
+  const float dl = a.delta[st];
+
+  // LDS offsets. K rows (sw2) and V rows (swr): row li, chunk 2 kk + g.
+  int koff[kKK32], voff[kKK32];
+#pragma unroll
+  for (int kk = 0; kk < kKK32; ++kk) {
+    koff[kk] = 16 * (li * kCPR + ((2 * kk + g) ^ sw2(li)));
+    voff[kk] = 16 * (li * kCPR + ((2 * kk + g) ^ swr(li)));
+  }
+  // K^T transposed reads (as the forward's V^T): lane t16 names row
+  // 4 g + t16 / 4 (+ 32 jt + 16 hh, + 8 for the upper 4 keys) and 4 columns at
+  // 32 dt + 16 vch + 4 (t16 % 4). sw2 of those rows depends on the +8 only.
+  const int t16 = lane & 15;
+  const int vch = (lane >> 4) & 1;
+  const int vrow = 4 * g + (t16 >> 2);
+  int klo[kDT], khi[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) {
+    const int chunk = (32 * dt + 16 * vch + 4 * (t16 & 3)) >> 3;
+    klo[dt] = 16 * (vrow * kCPR + (chunk ^ sw2(vrow))) + 8 * (t16 & 1);
+    khi[dt] = 16 * ((vrow + 8) * kCPR + (chunk ^ sw2(vrow + 8))) + 8 * (t16 & 1);
+  }
+
+  f32x16 dq[kDT];
+#pragma unroll
+  for (int dt = 0; dt < kDT; ++dt) dq[dt] = f32x16{};
+  const float c = a.c;
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int buf = t & 1;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      load_tile<true>(kg, (t + 1) * kBwdTile, N, k_lds[buf ^ 1], wave, lane);
+      load_tile<false>(vg, (t + 1) * kBwdTile, N, v_lds[buf ^ 1], wave, lane);
+    }
+    const int kv0 = t * kBwdTile;
+    const char* kb = reinterpret_cast<const char*>(k_lds[buf]);
+    const char* vb = reinterpret_cast<const char*>(v_lds[buf]);
+
+    // S^T = K Q^T and dP^T = V dO^T for two 32-key halves.
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < kKK32; ++kk) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * kCPR * 16);
+      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vb + voff[kk]);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vb + voff[kk] + 32 * kCPR * 16);
+      s0 = mfma32(k0, qf[kk], s0);
+      s1 = mfma32(k1, qf[kk], s1);
+      p0 = mfma32(v0, df[kk], p0);
+      p1 = mfma32(v1, df[kk], p1);
+    }
+    // dS^T = P^T (dP^T - delta); lane holds keys kv0 + 32 jt + 8 (r / 4) + 4 g + r % 4.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int o = 8 * (r >> 2) + 4 * g + (r & 3);
+      const int key0 = kv0 + o, key1 = kv0 + o + 32;
+      const bool v0 = key0 < N && qi < N && (!CAUSAL || key0 <= qi);
+      const bool v1 = key1 < N && qi < N && (!CAUSAL || key1 <= qi);
+      const float pa = v0 ? exp2_hw(fmaf(s0[r], c, -lse2)) : 0.f;
+      const float pb = v1 ? exp2_hw(fmaf(s1[r], c, -lse2)) : 0.f;
+      s0[r] = pa * (p0[r] - dl);
+      s1[r] = pb * (p1[r] - dl);
+    }
+    bf16x8 sb[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      sb[0][hh] = pack_bf16x8(s0[8 * hh + 0], s0[8 * hh + 1], s0[8 * hh + 2], s0[8 * hh + 3],
+                              s0[8 * hh + 4], s0[8 * hh + 5], s0[8 * hh + 6], s0[8 * hh + 7]);
+      sb[1][hh] = pack_bf16x8(s1[8 * hh + 0], s1[8 * hh + 1], s1[8 * hh + 2], s1[8 * hh + 3],
+                              s1[8 * hh + 4], s1[8 * hh + 5], s1[8 * hh + 6], s1[8 * hh + 7]);
+    }
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int jt = 0; jt < 2; ++jt)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int ro = (32 * jt + 16 * hh) * kCPR * 16;
+#pragma unroll
+        for (int dt = 0; dt < kDT; ++dt) {
+          const i16x4 lo = lds_read_tr(kb + klo[dt] + ro);
+          const i16x4 hi = lds_read_tr(kb + khi[dt] + ro);
+          dq[dt] = mfma32(join_bf16x8(lo, hi), sb[jt][hh], dq[dt]);
+        }
+      }
+  }
+
+  // Epilogue: lane holds row qi, columns 32 dt + 8 rq + 4 g + (0..3).
+  if (qi < N) {
+    uint16_t* row = a.dq + q_base + (size_t)qi * kD;
+    const float sc = a.scale;
+#pragma unroll
+    for (int dt = 0; dt < kDT; ++dt)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq)
+        *reinterpret_cast<uint2*>(row + 32 * dt + 8 * rq + 4 * g) =
+            pack_bf16x4(dq[dt][4 * rq + 0] * sc, dq[dt][4 * rq + 1] * sc, dq[dt][4 * rq + 2] * sc,
+                        dq[dt][4 * rq + 3] * sc);
+  }
+}
+
+hipError_t launch_bwd(const BwdArgs& a, bool causal, hipStream_t stream) {
+  const size_t rows = (size_t)a.B * a.Hq * a.Npad;
+  hipLaunchKernelGGL(fa_bwd_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int nwg_kv = a.B * a.Hkv * a.nkb;
+  const int nwg_q = a.B * a.Hq * a.nqb;
+  if (causal) {
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<true>, dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<true>, dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
+  } else {
+    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<false>, dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(fa_bwd_dq_kernel<false>, dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace fa

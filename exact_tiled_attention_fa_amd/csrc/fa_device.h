@@ -22,6 +22,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace fa {
@@ -163,6 +164,33 @@ __device__ __forceinline__ void merge_splits4(const float* __restrict__ op, cons
 
 // Threads per work-group of the merge kernels (D / 4 lanes per row).
 constexpr int kMergeThreads = 256;
+
+// 16 bytes per lane from global memory straight into LDS: lane l of the wave
+// fills bytes 16 l .. 16 l + 15 of the 1 KiB block whose LDS address goes in
+// M0; the global address is the uniform base plus the lane's 32-bit offset.
+// Issued through inline assembly so that the compiler's wait-count pass, which
+// cannot tell which LDS buffer a direct load writes, does not make LDS reads of
+// the other buffer wait for it; the kernel waits for its loads itself
+// (s_waitcnt vmcnt(0)) before the barrier that hands a buffer to its readers.
+// M0 is saved and restored around it.
+__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %2, %3\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(base)
+      : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
+}
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 // Work-group id -> logical id such that each XCD (work-groups are handed to
 // the 8 XCDs round-robin) receives one contiguous range of logical ids.

@@ -62,33 +62,6 @@ template <int D>
 __device__ __forceinline__ int vswz(int r) { return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2); }
 
 
-// 16 bytes per lane from global memory straight into LDS: lane l of the wave
-// fills bytes 16 l .. 16 l + 15 of the 1 KiB block whose LDS address goes in
-// M0; the global address is the uniform base plus the lane's 32-bit offset.
-// Issued through inline assembly so that the compiler's wait-count pass, which
-// cannot tell which LDS buffer a direct load writes, does not make LDS reads of
-// the other buffer wait for it; the kernel waits for its loads itself
-// (s_waitcnt vmcnt(0)) before the barrier that hands a buffer to its readers.
-// M0 is saved and restored around it.
-__device__ __forceinline__ void dma16(const void* base, uint32_t voff, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %2, %3\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "s"(lds), "v"(voff), "s"(base)
-      : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)((__attribute__((address_space(3))) const void*)p);
-}
-
-template <int V>
-using IC = std::integral_constant<int, V>;
-
 // The reference max of a row moves only when a tile's max exceeds it by more
 // than this many base-2 units; until then p = 2^(t - m) <= 2^8, and O and l are
 // rescaled together when it does move, so O / l and m + log2 l are unchanged.

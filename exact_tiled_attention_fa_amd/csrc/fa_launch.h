@@ -44,6 +44,36 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // Merge the key-split partials of a split forward into O (BF16) and lse.
 hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
+// Backward pass (d = 128): a row pass (lse2 = lse log2 e and delta = rowsum(dO O),
+// both padded to Npad rows with zeros), then dK/dV with one work-group per
+// (batch, KV head, 64-key block) sweeping the query tiles of every query head
+// of its group, and dQ with one work-group per (batch, query head, 128-row
+// block) sweeping the key tiles. Scores and weights are recomputed from Q, K
+// and lse; nothing N x N reaches memory.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* lse2;   // [B * Hq, Npad]
+  float* delta;  // [B * Hq, Npad]
+  int B, Hq, Hkv, N, Npad;
+  float c;       // scale * log2(e)
+  float scale;
+  int nkb;       // 64-key blocks per KV head
+  int nqb;       // 128-row query blocks per head
+};
+constexpr int kBwdKeyBlock = 64;
+constexpr int kBwdRowBlock = 128;
+constexpr int kBwdTile = 64;  // rows per Q/dO tile (dK/dV) and per K/V tile (dQ)
+
+hipError_t launch_bwd(const BwdArgs& a, bool causal, hipStream_t stream);
+
 // Split-KV decode: one work-group per (batch, KV head, head group, chunk).
 struct DecArgs {
   const uint16_t* q;

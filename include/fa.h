@@ -149,6 +149,36 @@ int fa_decode_varlen(const void* q, const void* k, const void* v, void* o, float
                      int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
                      void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
+/*
+ * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: two FP32
+ * values per query row (lse in base 2 and delta = rowsum(dO O)), each head's
+ * rows padded to a multiple of 64. 0 for invalid sizes.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int N, int d);
+
+/*
+ * fa_bwd -- backward pass of fa_fwd: given the upstream gradient dO, the
+ * gradients dQ, dK, dV of O = softmax(scale Q K^T) V (causal: key j visible to
+ * query i iff j <= i), recomputing the scores tile by tile from Q, K and the
+ * forward's lse ("Why is standard attention memory-bound, and how does
+ * FlashAttention fix it?", "Step 4: The result is exact, and the backward
+ * pass recomputes"). For GQA a KV head's dK, dV sum over the query heads that
+ * read it.
+ *
+ *   q, o, dout, dq [B, Hq,  N, d] bf16;  k, v, dk, dv [B, Hkv, N, d] bf16
+ *   lse            [B, Hq,  N]    fp32, natural log, as fa_fwd wrote it
+ *   d = 128 only (FA_ERR_HEAD_DIM otherwise).
+ *   workspace: device, 16-byte aligned, at least fa_bwd_workspace_bytes(B, Hq,
+ *   N, d) bytes, owned by the caller; contents on entry are ignored. Calls
+ *   sharing a workspace must be ordered.
+ *
+ * Every gradient is written once (no accumulation into the outputs). Three
+ * launches on `stream`: a row pass, dK/dV, dQ. Argument errors as fa_fwd.
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+           void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+           void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
 /* Human-readable name of a status code (static storage; never NULL). */
 const char* fa_status_string(int status);
 

@@ -74,3 +74,62 @@ def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str) -> float:
     assert np.isfinite(lse_gpu).all(), f"{what}: non-finite lse"
     assert worst <= LSE_REL, f"{what}: lse relative error {worst:.3e} > {LSE_REL}"
     return worst
+
+
+U_BF16 = 2.0 ** -8  # unit roundoff of an 8-bit significand
+
+
+def bwd_elem_bounds(q, k, v, do, causal, scale):
+    """Element-wise error bounds for the GPU backward pass (FP64 inputs; small sizes).
+
+    The kernels recompute P = 2^(S c - lse2) in FP32, round P and dS to BF16 for
+    the products dV = P^T dO and dK = dS^T Q (and dS for dQ = dS K), and take
+    delta_i = sum_t dO_it O_it from the forward's BF16 output O. With u = 2^-8:
+      * |O_gpu - O| <= 0.5 ulp(|O| (1 + 2^-7)) + 1.125 u (P|V|)   (the forward's bound),
+        so |delta_gpu - delta|_i <= E_i = sum_t |dO_it| (that bound)_it;
+      * dV: |err| <= 1.01 u (P^T |dO|) + 0.5 ulp + FP32 terms;
+      * dK: |err| <= |scale| ((P * E + u |dS|)^T |Q|) + 0.5 ulp + FP32 terms;
+      * dQ: |err| <= |scale| ((P * E + u |dS|) |K|) + 0.5 ulp + FP32 terms;
+    the FP32 terms (accumulation, exp2 and lse) take 1e-5 of the same sums with
+    |dP| + |delta| in place of the BF16 terms. The 0.5 ulp of the output's final
+    rounding is added by the caller (it needs the reference value).
+    Returns the bounds for dq [B,Hq,N,d], dk and dv [B,Hkv,N,d], without the ulp term.
+    """
+    from oracle import fa_oracle
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    bq = np.zeros((B, Hq, N, d))
+    bk = np.zeros((B, Hkv, N, d))
+    bv = np.zeros((B, Hkv, N, d))
+    u = U_BF16
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            qh, kh, vh, doh = q[b, h], k[b, g], v[b, g], do[b, h]
+            o, _, p = fa_oracle.attention_ref(qh[None, None], kh[None, None], vh[None, None], causal, scale,
+                                              return_p=True)
+            o, p = o[0, 0], p[0, 0]
+            pv_abs = p @ np.abs(vh)
+            e = (np.abs(doh) * (0.5 * ulp_bf16(np.abs(o) * (1 + 2.0 ** -7)) + 1.125 * u * pv_abs)).sum(1)
+            dp = doh @ vh.T
+            dlt = (p * dp).sum(1)
+            ds = p * (dp - dlt[:, None])
+            w_q = p * e[:, None] + u * np.abs(ds) + 1e-5 * p * (np.abs(dp) + np.abs(dlt)[:, None])
+            bq[b, h] = abs(scale) * (w_q @ np.abs(kh))
+            bk[b, g] += abs(scale) * (w_q.T @ np.abs(qh))
+            bv[b, g] += (1.01 * u + 1e-5) * (p.T @ np.abs(doh))
+    return bq, bk, bv
+
+
+def check_grad(name, got, ref, bound, what):
+    """got/ref/bound FP64 arrays of one gradient; bound excludes the final rounding."""
+    err = np.abs(got - ref)
+    full = bound + 0.5 * ulp_bf16(np.abs(ref) * (1 + 2.0 ** -7)) + 1e-6
+    ratio = float((err / full).max()) if err.size else 0.0
+    rel_rms = float(np.sqrt((err ** 2).sum() / max((ref ** 2).sum(), 1e-300))) if err.size else 0.0
+    print(f"    {what} {name}: max_abs {float(err.max()):.3e} rel_rms {rel_rms:.3e} elem_ratio {ratio:.3f}",
+          flush=True)
+    assert np.isfinite(got).all(), f"{what} {name}: non-finite values"
+    assert ratio <= 1.0, f"{what} {name}: element error {ratio:.3f} x its bound"
+    return ratio

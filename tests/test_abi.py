@@ -26,8 +26,9 @@ def lib():
 
 
 def test_header_declares_the_abi():
-    assert _declared_functions() == ["fa_decode", "fa_decode_varlen", "fa_decode_workspace_bytes", "fa_fwd",
-                                     "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_status_string"]
+    assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_varlen",
+                                     "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws",
+                                     "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -113,6 +114,28 @@ def dec_varlen(lib, lens=P, **kw):
 ])
 def test_decode_varlen_rejects(lib, kw, status):
     assert dec_varlen(lib, **kw) == status
+
+
+def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1, N=300, d=128, causal=0,
+        scale=0.1, ws=P, wsb=1 << 30):
+    return lib.fa_bwd(q, k, v, o, lse, do, dq, dk, dv, B, Hq, Hkv, N, d, causal, scale, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(do=None), -1), (dict(dk=None), -1), (dict(lse=None), -1),
+    (dict(N=0), -2), (dict(B=-1), -2), (dict(d=64), -3), (dict(d=96), -3), (dict(Hq=3, Hkv=2), -4),
+    (dict(dv=BAD), -5), (dict(do=BAD), -5), (dict(ws=BAD), -5), (dict(causal=3), -8),
+    (dict(scale=float("nan")), -8), (dict(ws=None), -6), (dict(wsb=64), -6),
+])
+def test_bwd_rejects(lib, kw, status):
+    assert bwd(lib, **kw) == status
+
+
+def test_bwd_workspace_size(lib):
+    # two floats per row, rows padded to 64 per head
+    assert lib.fa_bwd_workspace_bytes(1, 2, 300, 128) == (2 * 2 * 320 * 4 + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_bytes(1, 2, 300, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(0, 2, 300, 128) == 0
 
 
 def test_decode_workspace_size(lib):
