@@ -22,7 +22,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                                            untimed settle, for profilers:
                                            fwd-1x1x8192, fwd-1x1x8192-causal,
                                            fwd-1x32x4096, fwd-1x32x4096-causal,
-                                           fwd-1x8x131072-causal, decode)
+                                           fwd-1x8x131072-causal, decode,
+                                           bwd-1x32x4096, bwd-1x32x4096-causal)
 """
 from __future__ import annotations
 
@@ -118,6 +119,16 @@ def run_only(name: str, reps: int) -> None:
         lse = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
         fn = fa.prepare_fwd(q, k, v, o, lse, causal=case.causal, scale=case.scale)
         work = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
+        unit = "TFLOP/s"
+    elif name in ("bwd-1x32x4096", "bwd-1x32x4096-causal"):
+        case = si.HEADS32_4K_CAUSAL if name.endswith("causal") else si.HEADS32_4K
+        q, k, v = (up(x) for x in si.fwd_inputs(case))
+        g = up(si.normal_bf16(np.random.default_rng(case.seed + 10_000), (case.B, case.Hq, case.N, case.d)))
+        o, lse = fa.fwd(q, k, v, causal=case.causal, scale=case.scale)
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+        ws = torch.empty(fa.bwd_workspace_bytes(case.B, case.Hq, case.N, case.d), dtype=torch.uint8, device=dev)
+        fn = fa.prepare_bwd(q, k, v, o, lse, g, dq, dk, dv, ws, causal=case.causal, scale=case.scale)
+        work = 10.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
         unit = "TFLOP/s"
     elif name == "decode":
         case = si.DECODE_GQA
@@ -294,6 +305,23 @@ def main() -> int:
             extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
                           "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
             del q3, k3, v3, o3, l3
+        # Backward pass at the 32-head 4K shape: algorithmic FLOPs 10 N^2 d per head
+        # (five N x N x d products; halved causal), upstream gradient seeded.
+        for causal in (False, True):
+            case = si.HEADS32_4K_CAUSAL if causal else si.HEADS32_4K
+            q3, k3, v3 = (up(x) for x in si.fwd_inputs(case))
+            g3 = up(si.normal_bf16(np.random.default_rng(case.seed + 10_000), (case.B, case.Hq, case.N, case.d)))
+            o3, l3 = fa.fwd(q3, k3, v3, causal=causal, scale=case.scale)
+            dq3, dk3, dv3 = torch.empty_like(q3), torch.empty_like(k3), torch.empty_like(v3)
+            ws3 = torch.empty(fa.bwd_workspace_bytes(case.B, case.Hq, case.N, case.d), dtype=torch.uint8, device=dev)
+            run_b = fa.prepare_bwd(q3, k3, v3, o3, l3, g3, dq3, dk3, dv3, ws3, causal=causal, scale=case.scale)
+            settle(run_b, 0.2)
+            t = per_call_s(run_b, 10)
+            fl = 10.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if causal else 1)
+            key = "bwd_1x32x4096_d128" + ("_causal" if causal else "")
+            extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                          "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del q3, k3, v3, g3, o3, l3, dq3, dk3, dv3, ws3
         # Variable-length decode: the decode workload's shape, cache lengths drawn
         # uniformly from 1..8192 (seeded); bytes = the K/V rows actually read.
         vlens = np.random.default_rng(dcase.seed).integers(1, dcase.L + 1, size=dcase.B).astype(np.int32)
