@@ -127,9 +127,11 @@ def check_grad(name, got, ref, bound, what):
     err = np.abs(got - ref)
     full = bound + 0.5 * ulp_bf16(np.abs(ref) * (1 + 2.0 ** -7)) + 1e-6
     ratio = float((err / full).max()) if err.size else 0.0
-    rel_rms = float(np.sqrt((err ** 2).sum() / max((ref ** 2).sum(), 1e-300))) if err.size else 0.0
-    print(f"    {what} {name}: max_abs {float(err.max()):.3e} rel_rms {rel_rms:.3e} elem_ratio {ratio:.3f}",
-          flush=True)
+    ref_ss = float((ref ** 2).sum())
+    # (a gradient that is exactly zero, e.g. dQ and dK of a single key, has no relative error)
+    rel = f"{float(np.sqrt((err ** 2).sum() / ref_ss)):.3e}" if ref_ss > 0 else "n/a (zero reference)"
+    print(f"    {what} {name}: max_abs {float(err.max()) if err.size else 0.0:.3e} rel_rms {rel} "
+          f"elem_ratio {ratio:.3f}", flush=True)
     assert np.isfinite(got).all(), f"{what} {name}: non-finite values"
     assert ratio <= 1.0, f"{what} {name}: element error {ratio:.3f} x its bound"
     return ratio
