@@ -24,6 +24,10 @@ design notes):
     the library's argument checks, defined here for completeness).
   * GQA: query head h reads KV head h // (Hq // Hkv).
 
+The FP8 variant (attention_fp8_ref) is the same definition applied to the
+values of OCP FP8 E4M3 codes times per-tensor factors (fp8_e4m3_value decodes
+the codes from the format's bit layout).
+
 Parity: every function here is pinned by the CPU test-suite (the printed toy
 run of the online softmax, closed forms, invariants, brute force on tiny
 inputs and torch's FP64 CPU scaled_dot_product_attention).
@@ -282,6 +286,39 @@ def combine_ref(o_parts, lse_parts):
     o[dead] = 0.0
     lse = np.where(dead, -np.inf, m_safe + np.log(wsum_safe))
     return o, lse
+
+
+def fp8_e4m3_value(codes) -> np.ndarray:
+    """The value of each OCP FP8 E4M3 code (uint8), in float64.
+
+    Bit layout S.EEEE.MMM with exponent bias 7: E = 0 holds the subnormals
+    M 2^-9 (and signed zeros), E = 1..15 holds (1 + M/8) 2^(E-7), and
+    S.1111.111 is NaN (the format has no infinity, so E = 15 with M < 7 is
+    still finite: up to 448).
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0))
+    return np.where((c & 0x7F) == 0x7F, np.nan, sign * mag)
+
+
+def attention_fp8_ref(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float, causal: bool,
+                      scale: float, rows=None, return_p: bool = False):
+    """Exact attention of FP8-coded inputs with per-tensor dequantisation factors.
+
+    The 8-bit variant named in "Why is standard attention memory-bound, and how
+    does FlashAttention fix it?" ("What does FlashAttention-2 change?": the third
+    version adds FP8 low precision) changes the input format, not the result
+    being approximated: the inputs are the values q_scale * Q, k_scale * K and
+    v_scale * V of the E4M3 codes, and O and lse are the exact attention of
+    those values (attention_ref, in FP64).
+    """
+    q = fp8_e4m3_value(q8) * float(q_scale)
+    k = fp8_e4m3_value(k8) * float(k_scale)
+    v = fp8_e4m3_value(v8) * float(v_scale)
+    return attention_ref(q, k, v, causal, scale, rows=rows, return_p=return_p)
 
 
 def fwd_flops(N: int, d: int, causal: bool, heads: int = 1) -> float:

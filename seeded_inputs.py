@@ -49,6 +49,44 @@ def normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
     return bf16_round_bits(rng.standard_normal(size=shape, dtype=np.float32))
 
 
+# ---------------------------------------------------------------- FP8 E4M3 bits
+
+FP8_E4M3_MAX = 448.0  # largest finite OCP E4M3 value (1.75 x 2^8)
+
+
+def fp8_e4m3_round_bits(x: np.ndarray) -> np.ndarray:
+    """Round values to OCP FP8 E4M3 ("E4M3FN": 4 exponent bits, bias 7, 3
+    mantissa bits, subnormals, no infinity, NaN = S.1111.111); nearest, ties
+    to even; magnitudes above 448 saturate to 448. Returns uint8 codes.
+
+    Normal codes hold (1 + m/8) 2^(e-7) for e = 1..15; subnormal codes hold
+    m 2^-9 for e = 0, so the subnormal step 2^-9 continues into the first
+    normal binade and one rounding rule covers both.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), FP8_E4M3_MAX)
+    sign = np.signbit(x).astype(np.uint8) << 7
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -6)))           # binade (>= -6: subnormals share it)
+    step = 2.0 ** (e - 3)                                      # spacing of codes in that binade
+    k = np.rint(a / step)                                      # ties to even
+    e = np.where(k >= 16, e + 1, e)                            # rounded up into the next binade
+    k = np.where(k >= 16, k / 2, k)
+    normal = k >= 8
+    code = np.where(normal, ((e + 7).astype(np.int64) << 3) | (k.astype(np.int64) - 8),
+                    k.astype(np.int64))
+    code = np.where(np.isnan(x), 0x7F, code)
+    return (code.astype(np.uint8) | np.where(np.isnan(x), 0, sign)).astype(np.uint8)
+
+
+def quantize_fp8(rng: np.random.Generator, shape):
+    """One N(0,1) float32 draw quantised per tensor: (codes, descale) with the
+    values codes * descale and descale = max|x| / 448 (so max|x| maps to 448)."""
+    x = rng.standard_normal(size=shape, dtype=np.float32).astype(np.float64)
+    amax = float(np.abs(x).max()) if x.size else 1.0
+    descale = np.float32(amax / FP8_E4M3_MAX if amax > 0 else 1.0)
+    return fp8_e4m3_round_bits(x / float(descale)), float(descale)
+
+
 # ---------------------------------------------------------------- workloads
 
 @dataclasses.dataclass(frozen=True)
@@ -103,6 +141,17 @@ def fwd_inputs(case: FwdCase):
     k = normal_bf16(rng, (case.B, case.Hkv, case.N, case.d))
     v = normal_bf16(rng, (case.B, case.Hkv, case.N, case.d))
     return q, k, v
+
+
+def fwd_fp8_inputs(case: FwdCase):
+    """(q, k, v, q_scale, k_scale, v_scale): FP8 E4M3 code arrays of a forward
+    workload's shapes and their per-tensor dequantisation factors, drawn Q, K,
+    V in order (N(0,1) float32, each scaled so its largest magnitude is 448)."""
+    rng = np.random.default_rng(case.seed)
+    q, qs = quantize_fp8(rng, (case.B, case.Hq, case.N, case.d))
+    k, ks = quantize_fp8(rng, (case.B, case.Hkv, case.N, case.d))
+    v, vs = quantize_fp8(rng, (case.B, case.Hkv, case.N, case.d))
+    return q, k, v, qs, ks, vs
 
 
 def decode_inputs(case: DecodeCase):
