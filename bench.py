@@ -23,7 +23,8 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                                            fwd-1x1x8192, fwd-1x1x8192-causal,
                                            fwd-1x32x4096, fwd-1x32x4096-causal,
                                            fwd-1x8x131072-causal, decode,
-                                           bwd-1x32x4096, bwd-1x32x4096-causal)
+                                           bwd-1x32x4096, bwd-1x32x4096-causal,
+                                           fwd-fp8-1x32x4096, fwd-fp8-1x32x4096-causal)
 """
 from __future__ import annotations
 
@@ -42,6 +43,7 @@ if ROOT not in sys.path:
 METRIC = "attention fwd TFLOP/s & % BF16 MFMA peak (N=8K,d=128); decode HBM GB/s"
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_1x1x8192_d128_counters.txt")
 KERNEL_SOURCES = ["fa_fwd.hip", "fa_device.h", "fa_launch.h"]
 
@@ -118,6 +120,15 @@ def run_only(name: str, reps: int) -> None:
         o = torch.empty_like(q)
         lse = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
         fn = fa.prepare_fwd(q, k, v, o, lse, causal=case.causal, scale=case.scale)
+        work = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
+        unit = "TFLOP/s"
+    elif name in ("fwd-fp8-1x32x4096", "fwd-fp8-1x32x4096-causal"):
+        case = si.HEADS32_4K_CAUSAL if name.endswith("causal") else si.HEADS32_4K
+        q8, k8, v8, qs, ks, vs = si.fwd_fp8_inputs(case)
+        q, k, v = (torch.from_numpy(x).to(dev).view(torch.float8_e4m3fn) for x in (q8, k8, v8))
+        o = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        lse = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
+        fn = fa.prepare_fwd_fp8(q, k, v, qs, ks, vs, o, lse, causal=case.causal, scale=case.scale)
         work = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
         unit = "TFLOP/s"
     elif name in ("bwd-1x32x4096", "bwd-1x32x4096-causal"):
@@ -304,6 +315,21 @@ def main() -> int:
             key = "fwd_1x32x4096_d128" + ("_causal" if case.causal else "")
             extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
                           "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+            del q3, k3, v3, o3, l3
+        # FP8 forward at the 32-head 4K shape (E4M3 inputs quantised per tensor from
+        # the same seeded draws); the peak it is quoted against is the FP8 one.
+        for case in (si.HEADS32_4K, si.HEADS32_4K_CAUSAL):
+            q8, k8, v8, qs, ks, vs = si.fwd_fp8_inputs(case)
+            q3, k3, v3 = (torch.from_numpy(x).to(dev).view(torch.float8_e4m3fn) for x in (q8, k8, v8))
+            o3 = torch.empty(q3.shape, dtype=torch.bfloat16, device=dev)
+            l3 = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
+            run8 = fa.prepare_fwd_fp8(q3, k3, v3, qs, ks, vs, o3, l3, causal=case.causal, scale=case.scale)
+            settle(run8, 0.2)
+            t = per_call_s(run8, 10)
+            fl = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
+            key = "fwd_fp8_1x32x4096_d128" + ("_causal" if case.causal else "")
+            extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
+                          "frac_fp8_peak": round(fl / t / 1e12 / PEAK_FP8_TFLOPS, 4)}
             del q3, k3, v3, o3, l3
         # Backward pass at the 32-head 4K shape: algorithmic FLOPs 10 N^2 d per head
         # (five N x N x d products; halved causal), upstream gradient seeded.

@@ -5,6 +5,7 @@ kernels for gfx950). torch supplies device memory and the current stream
 only; every step of the computation runs in the library's kernels.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
+    o, lse = fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None)
     o, lse = decode(q, k, v, num_splits=16, scale=None)
 """
 from __future__ import annotations
@@ -16,8 +17,8 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes", "bwd_workspace_bytes",
-           "prepare_fwd", "prepare_decode", "prepare_bwd",
+__all__ = ["fwd", "fwd_fp8", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes",
+           "bwd_workspace_bytes", "prepare_fwd", "prepare_fwd_fp8", "prepare_decode", "prepare_bwd",
            "FaError"]
 
 
@@ -63,6 +64,66 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
                            B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(q.device))
     _lib.check(st, "fa_fwd")
     return out, lse
+
+
+_FP8_DTYPES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+
+
+def _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale):
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.device.type != "cuda" or t.dim() != 4 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous 4-D GPU tensor")
+        if t.dtype not in _FP8_DTYPES:
+            raise TypeError(f"{name} must hold E4M3 codes (torch.float8_e4m3fn or uint8; got {t.dtype})")
+    B, Hq, N, d = q.shape
+    Hkv = k.shape[1]
+    if k.shape != (B, Hkv, N, d) or v.shape != k.shape:
+        raise ValueError(f"k and v must be [B,Hkv,N,d] = {(B, Hkv, N, d)}; got {tuple(k.shape)}, {tuple(v.shape)}")
+    _check_bf16("out", out, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d)
+    return (q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_scale), float(k_scale), float(v_scale),
+            out.data_ptr(), lse.data_ptr(), B, Hq, Hkv, N, d, 1 if causal else 0, float(scale))
+
+
+def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k_scale: float, v_scale: float,
+            causal: bool = False, scale: float | None = None, out: torch.Tensor | None = None,
+            lse: torch.Tensor | None = None):
+    """FP8 attention forward (d = 128): q [B,Hq,N,d], k/v [B,Hkv,N,d] of OCP E4M3 codes
+    (torch.float8_e4m3fn or uint8) whose values are q_scale*q, k_scale*k, v_scale*v
+    -> (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32)."""
+    B, Hq, N, _ = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    st = _lib.lib().fa_fwd_fp8(*_fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale),
+                               _stream_handle(q.device))
+    _lib.check(st, "fa_fwd_fp8")
+    return out, lse
+
+
+def prepare_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, causal: bool = False,
+                    scale: float | None = None):
+    """Like prepare_fwd, for fwd_fp8 (one fa_fwd_fp8_ws call per invocation)."""
+    args = _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale)
+    B, Hq, N, d = q.shape
+    need = fwd_workspace_bytes(B, Hq, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    fn = _lib.lib().fa_fwd_fp8_ws
+    tail = (ws.data_ptr() if ws is not None else None, need)
+    device = q.device
+
+    def call():
+        st = fn(*args, *tail, torch.cuda.current_stream(device).cuda_stream)
+        if st:
+            _lib.check(st, "fa_fwd_fp8_ws")
+    call.workspace = ws
+    return call
 
 
 def fwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:

@@ -37,6 +37,10 @@ def _declare(lib):
     lib.fa_fwd_workspace_bytes.restype = sz
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_fwd_ws.restype = i
+    lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_fp8_ws.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
+    lib.fa_fwd_fp8_ws.restype = i
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
     lib.fa_decode_workspace_bytes.restype = sz
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]

@@ -148,6 +148,7 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.split_tiles = p.split_tiles;
   a.o_part = static_cast<float*>(ws);
   a.lse_part = ws ? a.o_part + (size_t)B * Hq * N * p.n_splits * d : nullptr;
+  a.v_scale = 1.f;
   hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
   if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, d, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
@@ -189,6 +190,78 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   void* ws = nullptr;
   if (hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
   st = launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
+}
+
+namespace {
+
+int check_fp8_args(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
+                   void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
+  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if (d != 128) return FA_ERR_HEAD_DIM;
+  if (!isfinite(q_scale) || !isfinite(k_scale) || !isfinite(v_scale) ||
+      !isfinite((double)scale * q_scale * k_scale * fa::kLog2eHost) ||
+      !isfinite((float)((double)scale * q_scale * k_scale * fa::kLog2eHost)))
+    return FA_ERR_ARG;
+  return check_fwd_sizes(B, Hq, N, d);
+}
+
+int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const void* v, float q_scale,
+                           float k_scale, float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                           int causal, float scale, void* ws, hipStream_t s) {
+  fa::FwdArgs a;
+  a.q = static_cast<const uint16_t*>(q);  // E4M3 bytes; the kernel reads them as such
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = static_cast<uint16_t*>(o);
+  a.lse = lse;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N;
+  a.c = (float)((double)scale * q_scale * k_scale * fa::kLog2eHost);
+  a.rows = p.rows;
+  a.nqb = p.nqb;
+  a.nwg = (int)p.nwg;
+  a.n_splits = p.n_splits;
+  a.split_tiles = p.split_tiles;
+  a.o_part = static_cast<float*>(ws);
+  a.lse_part = ws ? a.o_part + (size_t)B * Hq * N * p.n_splits * 128 : nullptr;
+  a.v_scale = v_scale;
+  hipError_t e = fa::launch_fwd_fp8(a, causal != 0, s);
+  if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, 128, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" int fa_fwd_fp8_ws(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                             float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d,
+                             int causal, float scale, void* workspace, size_t workspace_bytes,
+                             fa_stream_t stream) {
+  const int st = check_fp8_args(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale,
+                                p.ws_bytes > 0 ? workspace : nullptr, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale,
+                          float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal,
+                          float scale, fa_stream_t stream) {
+  int st = check_fp8_args(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (p.ws_bytes == 0)
+    return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale,
+                                  nullptr, s);
+  void* ws = nullptr;
+  if (hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
+  st = launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale, ws, s);
   const hipError_t ef = hipFreeAsync(ws, s);
   return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
 }

@@ -30,6 +30,7 @@ struct FwdArgs {
   int split_tiles;
   float* o_part;
   float* lse_part;
+  float v_scale;  // FP8 pass: the factor of V's codes (O = v_scale P V / l)
 };
 constexpr int kFwdKeys = 64;      // keys per K/V tile
 constexpr int kFwdWaveRows = 32;  // query rows per wave
@@ -41,6 +42,8 @@ constexpr int kFwdWaveRows = 32;  // query rows per wave
 inline int fwd_waves(bool causal, int N) { return causal && N < 16384 ? 4 : 8; }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
+// FP8 E4M3 inputs (q, k, v point at bytes), d = 128; c folds scale * q_scale * k_scale.
+hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t stream);
 // Merge the key-split partials of a split forward into O (BF16) and lse.
 hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 

@@ -100,6 +100,35 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               void* workspace, size_t workspace_bytes, fa_stream_t stream);
 
 /*
+ * fa_fwd_fp8 -- attention forward pass on FP8 inputs ("Why is standard
+ * attention memory-bound, and how does FlashAttention fix it?", follow-up
+ * "What does FlashAttention-2 change?": the third version adds 8-bit floating
+ * point low precision). Same operation as fa_fwd on the dequantised inputs:
+ *
+ *   q   [B, Hq,  N, d] uint8  OCP FP8 E4M3 codes; the query values are q_scale * Q
+ *   k   [B, Hkv, N, d] uint8  E4M3 codes; keys k_scale * K
+ *   v   [B, Hkv, N, d] uint8  E4M3 codes; values v_scale * V
+ *   o   [B, Hq,  N, d] bf16   output, rounded to nearest even
+ *   lse [B, Hq,  N]    fp32   natural-log logsumexp of scale * q.k (dequantised)
+ *
+ * d must be 128 (FA_ERR_HEAD_DIM otherwise). q_scale, k_scale, v_scale and
+ * scale * q_scale * k_scale must be finite (FA_ERR_ARG otherwise); any sign.
+ * Arithmetic: Q.K products exact, accumulated by the FP8 matrix cores; the
+ * weights 2^(t - m + 6) are rounded to E4M3 (relative error <= 2^-4) for the
+ * P V product while the row sums use their FP32 values; O and lse otherwise
+ * as fa_fwd. Key splits, their temporary buffer and the errors are those of
+ * fa_fwd (the workspace size is fa_fwd_workspace_bytes(B, Hq, N, 128)).
+ */
+int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
+               void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+               fa_stream_t stream);
+
+/* fa_fwd_fp8_ws -- fa_fwd_fp8 with a caller-owned workspace, as fa_fwd_ws. */
+int fa_fwd_fp8_ws(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
+                  void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                  void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
  * fa_decode_workspace_bytes -- size of the caller-provided workspace that
  * fa_decode needs for these sizes: FP32 partial outputs [B, Hq, S, d] and
  * partial logsumexps [B, Hq, S], S = number of non-empty chunks. Returns 0 for

@@ -27,8 +27,8 @@ def lib():
 
 def test_header_declares_the_abi():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_varlen",
-                                     "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_workspace_bytes", "fa_fwd_ws",
-                                     "fa_status_string"]
+                                     "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_ws",
+                                     "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -153,3 +153,36 @@ def test_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
     with pytest.raises(ValueError, match="GPU"):
         fa.fwd(x, x, x)
+
+
+def fwd_fp8(lib, q=P, k=P, v=P, qs=0.01, ks=0.01, vs=0.01, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128,
+            causal=0, scale=0.125):
+    return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1),
+    (dict(B=0), -2), (dict(N=-1), -2),
+    (dict(d=64), -3), (dict(d=96), -3),
+    (dict(Hq=5, Hkv=2), -4),
+    (dict(k=BAD), -5), (dict(lse=P + 1), -5),
+    (dict(causal=3), -8), (dict(scale=float("nan")), -8),
+    (dict(qs=float("inf")), -8), (dict(ks=float("nan")), -8), (dict(vs=float("-inf")), -8),
+    (dict(qs=1e30, ks=1e30), -8),   # scale * q_scale * k_scale overflows FP32
+    (dict(B=1 << 20, Hq=1 << 12, N=1 << 20), -2),
+])
+def test_fwd_fp8_rejects(lib, kw, status):
+    assert fwd_fp8(lib, **kw) == status
+
+
+def test_fwd_fp8_ws_rejects(lib):
+    args = dict(q=P, k=P, v=P, qs=0.01, ks=0.01, vs=0.01, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128,
+                causal=0, scale=0.125)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.fa_fwd_fp8_ws(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"],
+                                 a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], P, 0, None)
+    assert call(q=None) == -1
+    assert call(d=64) == -3
+    assert call(vs=float("nan")) == -8
