@@ -109,7 +109,7 @@ struct FwdPlan {
 // than kMinSplitTiles key tiles per split.
 FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal) {
   FwdPlan p;
-  const int waves = fa::fwd_waves(causal, N);
+  const int waves = fa::fwd_waves(causal, N, (int64_t)B * Hq * ((N + 255) / 256), device_cu_count());
   p.rows = fa::kFwdWaveRows * waves;
   p.nqb = (N + p.rows - 1) / p.rows;
   const int64_t base = (int64_t)B * Hq * p.nqb;

@@ -62,6 +62,12 @@ def test_long_context_128k_causal():
     _run_case(si.LONG_128K)
 
 
+def test_causal_8k_many_heads():
+    """8 heads of 8K causal: enough 256-row blocks to fill the CUs, so the
+    8-wave kernel runs unsplit (the 1-head 8K causal case takes the split path)."""
+    _run_case(si.FwdCase("1x8x8192 d128 causal", 1, 8, 8, 8192, 128, True, seed=41, sampled_rows=256))
+
+
 @pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
