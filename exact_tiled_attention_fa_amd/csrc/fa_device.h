@@ -128,6 +128,37 @@ template <int D>
 __device__ __forceinline__ void merge_splits4(const float* __restrict__ op, const float* __restrict__ lp, int S,
                                               uint16_t* __restrict__ o4, float* __restrict__ lse_out,
                                               bool write_lse) {
+  if (S <= 8) {
+    // One round trip: the partials do not depend on the lse values, so all
+    // sixteen loads go out together.
+    float l[8];
+    float4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const bool in = u < S;
+      l[u] = in ? lp[u] : -INFINITY;
+      v[u] = in ? *reinterpret_cast<const float4*>(op + (size_t)u * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    float M = l[0];
+#pragma unroll
+    for (int u = 1; u < 8; ++u) M = fmaxf(M, l[u]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float wsum = 0.f;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float w = u < S ? exp2_hw((l[u] - Ms) * kLog2e) : 0.f;
+      wsum += w;
+      acc.x = fmaf(w, v[u].x, acc.x);
+      acc.y = fmaf(w, v[u].y, acc.y);
+      acc.z = fmaf(w, v[u].z, acc.z);
+      acc.w = fmaf(w, v[u].w, acc.w);
+    }
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+    *reinterpret_cast<uint2*>(o4) = pack_bf16x4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+    if (write_lse) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += 8) {
     float l[8];
