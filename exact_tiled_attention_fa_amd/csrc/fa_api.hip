@@ -125,7 +125,8 @@ FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal) {
   }
   p.nwg = base * p.n_splits;
   const size_t rows = (size_t)B * Hq * N;
-  const size_t bytes = p.n_splits > 1 ? rows * p.n_splits * ((size_t)d + 1) * sizeof(float) : 0;
+  // BF16 partial outputs, then FP32 partial lse values.
+  const size_t bytes = p.n_splits > 1 ? rows * p.n_splits * ((size_t)d * 2 + sizeof(float)) : 0;
   p.ws_bytes = (bytes + 255) & ~(size_t)255;
   return p;
 }
@@ -146,8 +147,8 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.nwg = (int)p.nwg;
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
-  a.o_part = static_cast<float*>(ws);
-  a.lse_part = ws ? a.o_part + (size_t)B * Hq * N * p.n_splits * d : nullptr;
+  a.o_part = static_cast<uint16_t*>(ws);
+  a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = 1.f;
   hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
   if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, d, causal != 0, s);
@@ -224,8 +225,8 @@ int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const
   a.nwg = (int)p.nwg;
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
-  a.o_part = static_cast<float*>(ws);
-  a.lse_part = ws ? a.o_part + (size_t)B * Hq * N * p.n_splits * 128 : nullptr;
+  a.o_part = static_cast<uint16_t*>(ws);
+  a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * 128) : nullptr;
   a.v_scale = v_scale;
   hipError_t e = fa::launch_fwd_fp8(a, causal != 0, s);
   if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, 128, causal != 0, s);

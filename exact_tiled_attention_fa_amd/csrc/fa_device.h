@@ -117,27 +117,30 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
   return r;
 }
 
-// Log-sum-exp merge of the S normalised partial results of one row, for the
-// four columns col .. col + 3 a lane owns: M = max_s lse_s,
-// w_s = 2^((lse_s - M) log2 e), O = sum_s w_s O_s / sum_s w_s,
-// lse = M + ln sum_s w_s. op points at column col of partial 0 (partials D
-// floats apart), lp at the row's S lse values; the loads of up to eight
-// partials are in flight together. O goes to o4 (four BF16, nearest even);
-// lse is written when write_lse.
+// Log-sum-exp merge of one row's S key-split partials (BF16 normalised
+// outputs O_s and FP32 lse_s, natural log) for four columns: M = max_s lse_s,
+// w_s = e^(lse_s - M), O = sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s.
+// op points at column col of partial 0 (partials D values apart), lp at the
+// row's S lse values. With S <= 8 all loads go out together (the partials do
+// not depend on the lse values); otherwise eight partials at a time after a
+// first pass for M. O goes to o4 (four BF16, nearest even); lse is written
+// when write_lse.
 template <int D>
-__device__ __forceinline__ void merge_splits4(const float* __restrict__ op, const float* __restrict__ lp, int S,
+__device__ __forceinline__ void merge_splits4(const uint16_t* __restrict__ op, const float* __restrict__ lp, int S,
                                               uint16_t* __restrict__ o4, float* __restrict__ lse_out,
                                               bool write_lse) {
+  auto part = [&](int s) {
+    const uint2 w = *reinterpret_cast<const uint2*>(op + (size_t)s * D);
+    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  };
   if (S <= 8) {
-    // One round trip: the partials do not depend on the lse values, so all
-    // sixteen loads go out together.
     float l[8];
     float4 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool in = u < S;
       l[u] = in ? lp[u] : -INFINITY;
-      v[u] = in ? *reinterpret_cast<const float4*>(op + (size_t)u * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = in ? part(u) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     float M = l[0];
 #pragma unroll
@@ -176,7 +179,7 @@ __device__ __forceinline__ void merge_splits4(const float* __restrict__ op, cons
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool in = s0 + u < S;
-      v[u] = in ? *reinterpret_cast<const float4*>(op + (size_t)(s0 + u) * D) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v[u] = in ? part(s0 + u) : make_float4(0.f, 0.f, 0.f, 0.f);
       w[u] = in ? exp2_hw((lp[s0 + u] - Ms) * kLog2e) : 0.f;
     }
 #pragma unroll

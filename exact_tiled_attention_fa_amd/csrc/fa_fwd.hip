@@ -72,9 +72,9 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_kernel(FwdArgs a) {
   using C = FwdCfg<D, W>;
   // K buffers 0, 1 then V buffers 0, 1; after the sweep each wave stages its
-  // output rows here for coalesced stores.
-  // (A tile is 128 d bytes, the FP32 staging of one wave's 32 rows as much.)
-  __shared__ uint4 smem[W < 4 ? 4 : W][C::TILE_CHUNKS];
+  // output rows here for coalesced stores (one wave's 32 BF16 rows take half
+  // a tile, so eight waves fit).
+  __shared__ uint4 smem[4][C::TILE_CHUNKS];
   uint4 (*k_lds)[C::TILE_CHUNKS] = smem;
   uint4 (*v_lds)[C::TILE_CHUNKS] = smem + 2;
 
@@ -373,12 +373,12 @@ void fa_fwd_kernel(FwdArgs a) {
     last(IC<1>{});
   }
 
-  // ---- epilogue: O = O / l, lse = (m + log2 l) ln 2. Unsplit: O rounded to
-  // BF16 (nearest even) to the output. Split: FP32 partials. Each wave stages
-  // its 32 rows in LDS (row-major, 16-byte or 8-byte units XOR-swizzled by row
-  // so that both the fragment-order writes and the row-order reads are free of
-  // bank conflicts), then stores whole rows: every store instruction writes
-  // 1 KiB of contiguous row segments.
+  // ---- epilogue: O = O / l, lse = (m + log2 l) ln 2. O is rounded to BF16
+  // (nearest even), to the output or, with key splits, to the split's
+  // normalised partial. Each wave stages its 32 rows in LDS (row-major, 8-byte
+  // units XOR-swizzled by row so that both the fragment-order writes and the
+  // row-order reads are free of bank conflicts), then stores whole rows: every
+  // store instruction writes 1 KiB of contiguous row segments.
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
@@ -388,55 +388,34 @@ void fa_fwd_kernel(FwdArgs a) {
     else a.lse_part[(head_row0 + qi) * a.n_splits + split] = lse_v;
   }
   __syncthreads();  // every wave is done with the K/V buffers
-  char* stage = reinterpret_cast<char*>(smem) + wave * (32 * D * 4);
-  if (a.n_splits == 1) {
-    // 8-byte units: unit e = 8 dt + 2 rq + g of row li (columns 4 e .. 4 e + 3).
+  char* stage = reinterpret_cast<char*>(smem) + wave * (32 * D * 2);
+  // 8-byte units: unit e = 8 dt + 2 rq + g of row li (columns 4 e .. 4 e + 3).
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
+  for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int e = 8 * dt + 2 * rq + g;
-        const int pe = e ^ (D == 128 ? li : ((li >> 1) & 15));
-        *reinterpret_cast<uint2*>(stage + li * (D * 2) + 8 * pe) =
-            pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
-                        oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-      }
-    wave_sync_lds();
-    // Row order: lane l takes 16-byte chunk l % (D / 8) of row l / (D / 8) + RPI i.
-    constexpr int CPR16 = D / 8;
-    constexpr int RPI = 64 / CPR16;
-    const int c16 = lane % CPR16;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / CPR16;
-      const int sw = D == 128 ? r : ((r >> 1) & 15);
-      uint4 w = *reinterpret_cast<const uint4*>(stage + r * (D * 2) + 16 * (c16 ^ (sw >> 1)));
-      if (sw & 1) w = make_uint4(w.z, w.w, w.x, w.y);
-      const int row = q0 + wave * 32 + r;
-      if (row < N) *reinterpret_cast<uint4*>(a.o + qo_base + (size_t)row * D + 8 * c16) = w;
+    for (int rq = 0; rq < 4; ++rq) {
+      const int e = 8 * dt + 2 * rq + g;
+      const int pe = e ^ (D == 128 ? li : ((li >> 1) & 15));
+      *reinterpret_cast<uint2*>(stage + li * (D * 2) + 8 * pe) =
+          pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
+                      oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
     }
-  } else {
-    // 16-byte units: chunk c = 8 dt + 2 rq + g of row li.
-    constexpr int CPR = D / 4;  // 16-byte chunks per FP32 row
+  wave_sync_lds();
+  // Row order: lane l takes 16-byte chunk l % (D / 8) of row l / (D / 8) + RPI i,
+  // to the output or (split) to the split's partial row.
+  constexpr int CPR16 = D / 8;
+  constexpr int RPI = 64 / CPR16;
+  const int c16 = lane % CPR16;
+  uint16_t* const dst = a.n_splits == 1 ? a.o + qo_base : a.o_part + (head_row0 * a.n_splits + split) * D;
+  const size_t row_stride = (size_t)a.n_splits * D;
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int cc = 8 * dt + 2 * rq + g;
-        *reinterpret_cast<float4*>(stage + li * (D * 4) + 16 * (cc ^ (li % CPR))) =
-            make_float4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
-                        oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-      }
-    wave_sync_lds();
-    constexpr int RPI = 64 / CPR;
-    const int cc = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / CPR;
-      const float4 w = *reinterpret_cast<const float4*>(stage + r * (D * 4) + 16 * (cc ^ (r % CPR)));
-      const int row = q0 + wave * 32 + r;
-      if (row < N) *reinterpret_cast<float4*>(a.o_part + ((head_row0 + row) * a.n_splits + split) * D + 4 * cc) = w;
-    }
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / CPR16;
+    const int sw = D == 128 ? r : ((r >> 1) & 15);
+    uint4 w = *reinterpret_cast<const uint4*>(stage + r * (D * 2) + 16 * (c16 ^ (sw >> 1)));
+    if (sw & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+    const int row = q0 + wave * 32 + r;
+    if (row < N) *reinterpret_cast<uint4*>(dst + (size_t)row * row_stride + 8 * c16) = w;
   }
 }
 

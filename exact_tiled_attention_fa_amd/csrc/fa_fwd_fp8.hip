@@ -82,8 +82,8 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   constexpr int RPB = 1024 / kD8;         // rows per block
   constexpr int DT = kD8 / 32;            // 32-wide d tiles of O^T
   // K buffers 0, 1 then V buffers 0, 1 (8 KiB each); after the sweep the
-  // epilogue stages each wave's rows over the whole array.
-  constexpr int STAGE_BYTES = W * 32 * kD8 * 4;
+  // epilogue stages each wave's 32 BF16 rows (8 KiB) over the whole array.
+  constexpr int STAGE_BYTES = W * 32 * kD8 * 2 > 4 * kTile8 ? W * 32 * kD8 * 2 : 4 * kTile8;
   __shared__ uint4 smem[STAGE_BYTES / 16];
   char* const lds = reinterpret_cast<char*>(smem);
   auto k_lds = [&](int i) { return lds + i * kTile8; };
@@ -345,7 +345,8 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     last(IC<1>{});
   }
 
-  // ---- epilogue (as the BF16 pass): O = v_scale O / l, lse = (m - 6 + log2 l) ln 2.
+  // ---- epilogue (as the BF16 pass): O = v_scale O / l, lse = (m - 6 + log2 l) ln 2;
+  // O rounded to BF16 to the output or, with key splits, to the split's partial.
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? a.v_scale / l_tot : 0.f;
   const float lse_v = l_tot > 0.f ? (m_run - kPBias8 + log2_hw(l_tot)) * kLn2 : -INFINITY;
@@ -356,51 +357,30 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     else a.lse_part[(head_row0 + qi) * a.n_splits + split] = lse_v;
   }
   __syncthreads();  // every wave is done with the K/V buffers
-  char* stage = lds + wave * (32 * kD8 * 4);
-  if (a.n_splits == 1) {
-    // 8-byte units: unit e = 8 dt + 2 rq + g of row li (columns 4 e .. 4 e + 3).
+  char* stage = lds + wave * (32 * kD8 * 2);
+  // 8-byte units: unit e = 8 dt + 2 rq + g of row li (columns 4 e .. 4 e + 3).
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
+  for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int e = 8 * dt + 2 * rq + g;
-        *reinterpret_cast<uint2*>(stage + li * (kD8 * 2) + 8 * (e ^ li)) =
-            pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
-                        oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-      }
-    wave_sync_lds();
-    constexpr int C16 = kD8 / 8;  // 16-byte chunks per BF16 row
-    constexpr int RPI = 64 / C16;
-    const int c16 = lane % C16;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / C16;
-      uint4 w = *reinterpret_cast<const uint4*>(stage + r * (kD8 * 2) + 16 * (c16 ^ (r >> 1)));
-      if (r & 1) w = make_uint4(w.z, w.w, w.x, w.y);
-      const int row = q0 + wave * 32 + r;
-      if (row < N) *reinterpret_cast<uint4*>(a.o + qo_base + (size_t)row * kD8 + 8 * c16) = w;
+    for (int rq = 0; rq < 4; ++rq) {
+      const int e = 8 * dt + 2 * rq + g;
+      *reinterpret_cast<uint2*>(stage + li * (kD8 * 2) + 8 * (e ^ li)) =
+          pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
+                      oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
     }
-  } else {
-    constexpr int CPR = kD8 / 4;  // 16-byte chunks per FP32 row
+  wave_sync_lds();
+  constexpr int C16 = kD8 / 8;  // 16-byte chunks per BF16 row
+  constexpr int RPI = 64 / C16;
+  const int c16 = lane % C16;
+  uint16_t* const dst = a.n_splits == 1 ? a.o + qo_base : a.o_part + (head_row0 * a.n_splits + split) * kD8;
+  const size_t row_stride = (size_t)a.n_splits * kD8;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        const int cc = 8 * dt + 2 * rq + g;
-        *reinterpret_cast<float4*>(stage + li * (kD8 * 4) + 16 * (cc ^ (li % CPR))) =
-            make_float4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
-                        oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
-      }
-    wave_sync_lds();
-    constexpr int RPI = 64 / CPR;
-    const int cc = lane % CPR;
-#pragma unroll
-    for (int i = 0; i < 32 / RPI; ++i) {
-      const int r = RPI * i + lane / CPR;
-      const float4 w = *reinterpret_cast<const float4*>(stage + r * (kD8 * 4) + 16 * (cc ^ (r % CPR)));
-      const int row = q0 + wave * 32 + r;
-      if (row < N) *reinterpret_cast<float4*>(a.o_part + ((head_row0 + row) * a.n_splits + split) * kD8 + 4 * cc) = w;
-    }
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = RPI * i + lane / C16;
+    uint4 w = *reinterpret_cast<const uint4*>(stage + r * (kD8 * 2) + 16 * (c16 ^ (r >> 1)));
+    if (r & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+    const int row = q0 + wave * 32 + r;
+    if (row < N) *reinterpret_cast<uint4*>(dst + (size_t)row * row_stride + 8 * c16) = w;
   }
 }
 

@@ -12,8 +12,8 @@ constexpr float kLog2eHost = 1.4426950408889634f;
 // Forward pass: one work-group per (batch, query head, key split, 128-row
 // query block). With n_splits == 1 each work-group sweeps all keys of its
 // block and writes O and lse; otherwise split s covers key tiles
-// [s * split_tiles, (s + 1) * split_tiles) and writes an FP32 normalised
-// partial O_s and its lse_s to o_part [B*Hq*N, n_splits, d] and
+// [s * split_tiles, (s + 1) * split_tiles) and writes its normalised partial
+// O_s (BF16) and lse_s (FP32) to o_part [B*Hq*N, n_splits, d] and
 // lse_part [B*Hq*N, n_splits] for fa_fwd_combine_kernel.
 struct FwdArgs {
   const uint16_t* q;
@@ -28,8 +28,8 @@ struct FwdArgs {
   int nwg;   // total work-groups
   int n_splits;
   int split_tiles;
-  float* o_part;
-  float* lse_part;
+  uint16_t* o_part;  // [B*Hq*N, n_splits, d] BF16 normalised partial outputs
+  float* lse_part;   // [B*Hq*N, n_splits] FP32
   float v_scale;  // FP8 pass: the factor of V's codes (O = v_scale P V / l)
 };
 constexpr int kFwdKeys = 64;      // keys per K/V tile

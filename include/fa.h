@@ -66,15 +66,16 @@ typedef enum {
  *   lse [B, Hq,  N]    fp32   natural-log logsumexp of each row's scaled scores
  *   causal: 0 = every key visible; 1 = key j visible to query i iff j <= i.
  *
- * d must be 64 or 128. One kernel launch per call, except when
- * B * Hq * ceil(N / 128) work-groups would leave the GPU's compute units idle:
- * then the keys of every query block are split across work-groups (at least
- * 512 keys per split, about two work-groups per compute unit), each writing an
- * FP32 normalised partial output and its logsumexp, and a second launch merges
- * them with the log-sum-exp combine. That path takes a stream-ordered
- * temporary buffer of B*Hq*N*splits*(d+1)*4 bytes from the device's default
- * memory pool (hipMallocAsync / hipFreeAsync on `stream`) and returns
- * FA_ERR_LAUNCH if the pool cannot supply it.
+ * d must be 64 or 128. One kernel launch per call, except when the query
+ * blocks (128 or 256 rows) would leave the GPU's compute units idle: then the
+ * keys of every query block are split across work-groups (at least 512 keys
+ * per split; as many work-groups as fit on the compute units at once), each
+ * writing its normalised partial output (BF16, rounded to nearest even) and
+ * logsumexp (FP32), and a second launch merges them with the log-sum-exp
+ * combine. That path takes a stream-ordered temporary buffer of
+ * B*Hq*N*splits*(2d+4) bytes from the device's default memory pool
+ * (hipMallocAsync / hipFreeAsync on `stream`) and returns FA_ERR_LAUNCH if the
+ * pool cannot supply it.
  */
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int Hq, int Hkv, int N, int d, int causal, float scale,
@@ -83,7 +84,7 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 /*
  * fa_fwd_workspace_bytes -- bytes of caller-provided workspace that fa_fwd_ws
  * needs for these sizes on the current device: 0 when the forward runs as one
- * launch, else the key-split partials (FP32 [B*Hq*N, splits, d] followed by
+ * launch, else the key-split partials (BF16 [B*Hq*N, splits, d] followed by
  * FP32 [B*Hq*N, splits]) rounded up to 256 bytes. Returns 0 for invalid sizes.
  */
 size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d);

@@ -17,6 +17,11 @@ Tolerances:
                            + 1.125 * 2^-8 (P|V|)_ref + 1e-6,
     where (P|V|)_ref is the oracle's attention output with V replaced by |V|.
   * internal, aggregate: relative RMS error of O <= 2^-8.
+  * key splits: when a call splits the keys, each split's normalised partial
+    O_c is rounded to BF16 before the log-sum-exp combine, which moves O_i by
+    at most 2^-8 sum_c w_c |O_c| / sum_c w_c <= 2^-8 (P|V|)_i (|O_c| <= the
+    split's own P|V|, and the weights w_c recombine those into P|V|); the
+    element bound then takes 2.125 * 2^-8 (P|V|) instead of 1.125.
 """
 import numpy as np
 import torch
@@ -46,17 +51,18 @@ def ulp_bf16(x: np.ndarray) -> np.ndarray:
     return 2.0 ** (np.floor(np.log2(ax)) - 7)
 
 
-def elem_bound(o_ref: np.ndarray, pabs_ref: np.ndarray) -> np.ndarray:
-    return 0.5 * ulp_bf16(np.abs(o_ref) * (1 + 2.0 ** -7)) + 1.125 * 2.0 ** -8 * pabs_ref + 1e-6
+def elem_bound(o_ref: np.ndarray, pabs_ref: np.ndarray, split: bool = False) -> np.ndarray:
+    k = 2.125 if split else 1.125
+    return 0.5 * ulp_bf16(np.abs(o_ref) * (1 + 2.0 ** -7)) + k * 2.0 ** -8 * pabs_ref + 1e-6
 
 
 def check_o(o_gpu: np.ndarray, o_ref: np.ndarray, pabs_ref: np.ndarray, what: str,
-            flat_gate: bool = True) -> dict:
+            flat_gate: bool = True, split: bool = False) -> dict:
     err = np.abs(o_gpu - o_ref)
     finite = bool(np.isfinite(o_gpu).all())
     max_abs = float(err.max()) if err.size else 0.0
     rel_rms = float(np.sqrt((err ** 2).sum() / max((o_ref ** 2).sum(), 1e-300))) if err.size else 0.0
-    worst = float((err / elem_bound(o_ref, pabs_ref)).max()) if err.size else 0.0
+    worst = float((err / elem_bound(o_ref, pabs_ref, split)).max()) if err.size else 0.0
     stats = {"max_abs": max_abs, "rel_rms": rel_rms, "elem_ratio": worst}
     print(f"    {what}: {stats}", flush=True)
     assert finite, f"{what}: non-finite O"

@@ -26,6 +26,8 @@ half-step of a 3-bit significand):
   * lse: |dlse| / max(|lse|, 1) <= 1e-3 (the BF16 pass's gate): the weights'
     rounding does not reach lse (l sums the FP32 values), the score error does,
     at most eps_i.
+  * key splits round each split's normalised partial to BF16 before the
+    combine: at most 2^-8 (P|V|)_i more (as for the BF16 pass).
 """
 import math
 import sys
@@ -54,8 +56,9 @@ def _upload(codes):
     return t.view(torch.float8_e4m3fn)
 
 
-def _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p):
-    """Element bound (without the output rounding) for O at the checked rows."""
+def _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p, split):
+    """Element bound (without the output rounding) for O at the checked rows;
+    with key splits the BF16 rounding of the partials adds 2^-8 (P|V|)."""
     B, Hq, R, N = p.shape
     Hkv = k8.shape[1]
     G = Hq // Hkv
@@ -73,7 +76,8 @@ def _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p):
             if causal:
                 sabs = np.where(np.arange(N)[None, :] <= ids[:, None], sabs, 0.0)
             eps = MFMA_F8_REL * abs(scale * qs * ks) * sabs.max(axis=1)
-            out[b, h] = e @ va + eps[:, None] * (ph @ va + np.abs(o_ref[b, h]))
+            pva = ph @ va
+            out[b, h] = e @ va + eps[:, None] * (pva + np.abs(o_ref[b, h])) + (2.0 ** -8 if split else 0.0) * pva
     return out
 
 
@@ -98,7 +102,8 @@ def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0
         lse_np = np.stack([lse_np[:, h, rows[h]] for h in range(Hq)], axis=1)
     o_ref, lse_ref, p = fa_oracle.attention_fp8_ref(q8, k8, v8, qs, ks, vs, causal, scale, rows=rows,
                                                     return_p=True)
-    bound = _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p)
+    split = fa.fwd_workspace_bytes(B, Hq, N, 128) > 0
+    bound = _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p, split)
     del p
     full = bound + 0.5 * ulp_bf16(np.abs(o_ref) * (1 + 2.0 ** -7)) + 1e-6
     err = np.abs(o_np - o_ref)
