@@ -154,7 +154,8 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 
   // ---- Q^T operand: lane (row li, half g) holds bytes 64 kk + 32 g .. + 31 of
   // its row. A negative scale product flips the sign bits (exact); a zero one
-  // becomes the smallest normal float (p = 1 for every visible key).
+  // becomes the smallest normal float (every visible key then gets the same
+  // weight, as with scale 0).
   const int qi = q0 + wave * 32 + li;
   const int sign = a.c < 0.f ? (int)0x80808080u : 0;
   const float c = fmaxf(fabsf(a.c), 1.17549435e-38f);
