@@ -94,6 +94,7 @@ __device__ __forceinline__ void combine_row(const float* __restrict__ o_part, co
 }
 
 constexpr int kDecWaveKeys = 32;
+constexpr int kDecRankedSeqs = kDecThreads;  // varlen batches ranked by length in the grid order
 constexpr int kDecStepKeys = 4 * kDecWaveKeys;
 
 template <int D>
@@ -120,15 +121,34 @@ void fa_decode_split_kernel(DecArgs a) {
   const int lane = tid & 63;
   const int wave = tid >> 6;
 
-  // Chunk index slowest: consecutive work-groups (dealt round-robin to the 8
-  // XCDs) take the same chunk of different sequences and heads, so every XCD
-  // gets an even share of each chunk index, also when per-sequence lengths
-  // leave the later chunks empty.
+  // Grid order. All caches of one length: chunk index slowest, so consecutive
+  // work-groups (dealt round-robin to the 8 XCDs) take the same chunk of
+  // different sequences and heads. Caches of their own lengths (up to
+  // kDecRankedSeqs sequences): sequences longest first, each with all its
+  // chunks and heads, so the longest chunks start first and the short ones
+  // fill in behind them; every work-group ranks the lengths itself.
   int rest = blockIdx.x;
   const int hg = rest % a.n_hg; rest /= a.n_hg;
   const int hk = rest % a.Hkv; rest /= a.Hkv;
-  const int b = rest % a.B;
-  const int split = rest / a.B;
+  int b, split;
+  if (a.lens && a.B <= kDecRankedSeqs) {
+    __shared__ int by_rank[kDecRankedSeqs];
+    if (tid < a.B) {
+      const int mine = min(max(a.lens[tid], 0), a.L);
+      int r = 0;
+      for (int j = 0; j < a.B; ++j) {
+        const int lj = min(max(a.lens[j], 0), a.L);
+        r += (lj > mine) || (lj == mine && j < tid);
+      }
+      by_rank[r] = tid;
+    }
+    __syncthreads();
+    split = rest % a.S;
+    b = by_rank[rest / a.S];
+  } else {
+    b = rest % a.B;
+    split = rest / a.B;
+  }
   // Keys of this sequence and its chunk: with per-sequence lengths the S
   // chunks cut each sequence's own keys, so the work follows the lengths.
   const int len = a.lens ? min(max(a.lens[b], 0), a.L) : a.L;
