@@ -44,13 +44,42 @@ __device__ __forceinline__ float wave_sum(float x) {
 // Log-sum-exp merge of S normalised partial results of one row, by one wave:
 // M = max_s lse_s, w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s,
 // lse = M + ln sum_s w_s. Partial s of the row is o_part[s * D ..]; its lse is
-// lse_part[s]. Lanes load the lse values in parallel; the weights are then
-// broadcast with readlane while each lane accumulates D / 64 columns.
+// lse_part[s]. Lanes load the lse values in parallel (with up to 16 partials,
+// together with all partial rows); the weights are then broadcast with
+// readlane while each lane accumulates D / 64 columns.
 template <int D>
 __device__ __forceinline__ void combine_row(const float* __restrict__ o_part, const float* __restrict__ lse_part,
                                             int S, uint16_t* __restrict__ o_row, float* __restrict__ lse_out) {
   constexpr int PER = D / 64;
   const int lane = __lane_id();
+  if (S <= 16) {
+    // One round trip: the partial rows do not depend on the lse values, so
+    // their loads go out with them.
+    const float l = lane < S ? lse_part[lane] : -INFINITY;
+    float v[16][PER];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int j = 0; j < PER; ++j) v[u][j] = u < S ? o_part[(size_t)u * D + lane * PER + j] : 0.f;
+    const float M = wave_max(l);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    const float wl = lane < S ? exp2_hw((l - Ms) * kLog2e) : 0.f;
+    float acc[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) acc[j] = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float w = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), u));
+#pragma unroll
+      for (int j = 0; j < PER; ++j) acc[j] = fmaf(w, v[u][j], acc[j]);
+    }
+    const float wsum = wave_sum(wl);
+    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) o_row[lane * PER + j] = __builtin_bit_cast(uint16_t, (__bf16)(acc[j] * inv));
+    if (lane == 0) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
+    return;
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += 64) M = fmaxf(M, s0 + lane < S ? lse_part[s0 + lane] : -INFINITY);
   M = wave_max(M);
