@@ -62,12 +62,12 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128 (128 for fa_bwd and fa_fwd_fp8)";
     case FA_ERR_GQA: return "FA_ERR_GQA: Hq must be a multiple of Hkv";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
-    case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0 or 1 and scale finite";
+    case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0 or 1 and the scales finite";
     default: return "unknown fa_status";
   }
 }

@@ -48,12 +48,12 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or num_splits out of range */
-  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 (fa_bwd, fa_fwd_fp8: not 128) */
   FA_ERR_GQA = -4,       /* Hq is not a multiple of Hkv */
   FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
   FA_ERR_LAUNCH = -7,    /* a HIP launch or allocation failed */
-  FA_ERR_ARG = -8        /* causal not 0/1, or scale not finite */
+  FA_ERR_ARG = -8        /* causal not 0/1, or a scale (factor) not finite */
 } fa_status;
 
 /*
