@@ -186,3 +186,12 @@ def test_fwd_fp8_ws_rejects(lib):
     assert call(q=None) == -1
     assert call(d=64) == -3
     assert call(vs=float("nan")) == -8
+
+
+def test_missing_library_raises(monkeypatch):
+    """No fallback path: without libfa.so every entry point raises."""
+    from exact_tiled_attention_fa_amd import _lib
+    monkeypatch.setattr(_lib, "LIB_PATH", os.path.join(ROOT, "no_such_dir", "libfa.so"))
+    monkeypatch.setattr(_lib, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        _lib.lib()
