@@ -5,6 +5,7 @@ kernels for gfx950). torch supplies device memory and the current stream
 only; every step of the computation runs in the library's kernels.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
+    o = attention(q, k, v, causal=False, scale=None)     # differentiable (backward: d = 128)
     o, lse = fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None)
     o, lse = decode(q, k, v, num_splits=16, scale=None)
 """
@@ -17,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["fwd", "fwd_fp8", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes",
+__all__ = ["attention", "fwd", "fwd_fp8", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes",
            "bwd_workspace_bytes", "prepare_fwd", "prepare_fwd_fp8", "prepare_decode", "prepare_bwd",
            "FaError"]
 
@@ -298,3 +299,28 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
         if st:
             _lib.check(st, name)
     return call
+
+
+class _Attention(torch.autograd.Function):
+    """fwd in the forward pass; bwd (from the saved O and lse) in the backward pass."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, causal, scale):
+        o, lse = fwd(q, k, v, causal=causal, scale=scale)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.causal = causal
+        ctx.scale = scale
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = bwd(q, k, v, o, lse, do.contiguous(), causal=ctx.causal, scale=ctx.scale)
+        return dq, dk, dv, None, None
+
+
+def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
+              scale: float | None = None) -> torch.Tensor:
+    """Differentiable attention: O = softmax(scale Q K^T) V (bf16 [B,Hq,N,d]) through
+    torch.autograd; gradients come from the library's backward pass (d = 128)."""
+    return _Attention.apply(q, k, v, bool(causal), scale)
