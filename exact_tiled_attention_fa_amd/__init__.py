@@ -5,7 +5,7 @@ kernels for gfx950). torch supplies device memory and the current stream
 only; every step of the computation runs in the library's kernels.
 
     o, lse = fwd(q, k, v, causal=False, scale=None)
-    o = attention(q, k, v, causal=False, scale=None)     # differentiable (backward: d = 128)
+    o = attention(q, k, v, causal=False, scale=None)     # differentiable
     o, lse = fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, causal=False, scale=None)
     o, lse = decode(q, k, v, num_splits=16, scale=None)
 """
@@ -210,7 +210,7 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace):
 def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse: torch.Tensor,
         dout: torch.Tensor, causal: bool = False, scale: float | None = None,
         workspace: torch.Tensor | None = None):
-    """Backward pass of fwd (d = 128): (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]) bf16, from the
+    """Backward pass of fwd (d = 64 or 128): (dq [B,Hq,N,d], dk, dv [B,Hkv,N,d]) bf16, from the
     forward's o and lse and the upstream gradient dout."""
     B, Hq, N, d = q.shape
     if workspace is None:
@@ -322,5 +322,5 @@ class _Attention(torch.autograd.Function):
 def attention(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
               scale: float | None = None) -> torch.Tensor:
     """Differentiable attention: O = softmax(scale Q K^T) V (bf16 [B,Hq,N,d]) through
-    torch.autograd; gradients come from the library's backward pass (d = 128)."""
+    torch.autograd; gradients come from the library's backward pass."""
     return _Attention.apply(q, k, v, bool(causal), scale)

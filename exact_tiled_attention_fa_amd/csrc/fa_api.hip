@@ -62,7 +62,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128 (128 for fa_bwd and fa_fwd_fp8)";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128 (128 for fa_fwd_fp8)";
     case FA_ERR_GQA: return "FA_ERR_GQA: Hq must be a multiple of Hkv";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
@@ -274,7 +274,7 @@ int64_t bwd_npad(int N) { return ((int64_t)N + fa::kBwdTile - 1) / fa::kBwdTile 
 }  // namespace
 
 extern "C" size_t fa_bwd_workspace_bytes(int B, int Hq, int N, int d) {
-  if (d != 128 || check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
+  if (check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
   const size_t bytes = (size_t)2 * B * Hq * (size_t)bwd_npad(N) * sizeof(float);
   return (bytes + 255) & ~(size_t)255;
 }
@@ -285,7 +285,6 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   if (!o || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
   int st = check_fwd_args(q, k, v, dq, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_ERR_HEAD_DIM;
   if (!aligned16(o) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv)) return FA_ERR_ALIGN;
   if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
   const size_t need = fa_bwd_workspace_bytes(B, Hq, N, d);
@@ -315,7 +314,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.scale = scale;
   a.nkb = (int)nkb;
   a.nqb = (int)nqb;
-  const hipError_t e = fa::launch_bwd(a, causal != 0, reinterpret_cast<hipStream_t>(stream));
+  const hipError_t e = fa::launch_bwd(a, d, causal != 0, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 

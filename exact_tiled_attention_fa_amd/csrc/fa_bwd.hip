@@ -1,4 +1,4 @@
-// Backward pass of exact attention for gfx950 (head dim 128).
+// Backward pass of exact attention for gfx950 (head dims 64 and 128).
 //
 // What it computes: with P = softmax(scale Q K^T) (masked when causal) and the
 // upstream gradient dO, the chain rule through O = P V gives
@@ -35,54 +35,72 @@ namespace fa {
 
 namespace {
 
-constexpr int kD = 128;
-constexpr int kCPR = kD / 8;                 // 16-byte chunks per row
-constexpr int kTileChunks = kBwdTile * kCPR;  // 16 KiB tiles
-constexpr int kKK32 = kD / 16;               // k-steps of a 32x32x16 product over d
-constexpr int kDT = kD / 32;                 // 32-wide d tiles
-constexpr int kKK16 = kD / 32;               // k-steps of a 16x16x32 product over d
-constexpr int kTT = kD / 16;                 // 16-wide d tiles
+template <int D>
+struct BwdCfg {
+  static constexpr int CPR = D / 8;                // 16-byte chunks per row
+  static constexpr int TILE_CHUNKS = kBwdTile * CPR;  // 64-row tiles (16 or 8 KiB)
+  static constexpr int KK32 = D / 16;              // k-steps of a 32x32x16 product over d
+  static constexpr int DT = D / 32;                // 32-wide d tiles
+  static constexpr int KK16 = D / 32;              // k-steps of a 16x16x32 product over d
+  static constexpr int TT = D / 16;                // 16-wide d tiles
+  static constexpr int RPB = 512 / D;              // rows per 1 KiB direct-load block
+  static constexpr int BPW = D / 32;               // blocks per wave per tile (4 waves)
+};
 
-// XOR swizzle of the 16-byte chunk index of tile row r. Bijective on r & 15,
-// so 16 consecutive rows read at one chunk hit 16 different bank groups; and
-// for the transposed reads (4 consecutive rows from a 4-aligned start, two
-// adjacent chunks) it takes 8 different values. Rows 16 apart share it.
-__device__ __forceinline__ int sw2(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+// XOR swizzle of the 16-byte chunk index of tile row r, for tiles read both
+// by rows (16 consecutive rows at one chunk) and transposed (4 rows from a
+// 4-aligned start, two adjacent chunks); rows 16 apart share it, so row
+// offsets that are multiples of 16 stay immediates.
+//   d = 128 (16 chunks, a row spans the 64 banks): bijective on r & 15 and
+//   8-valued on a transposed read's rows.
+//   d = 64 (8 chunks, two rows per 64 banks, so row parity separates them):
+//   a bit permutation of t = (r >> 1) & 7 (t0 -> bit 1, t1 -> bit 2, t2 ->
+//   bit 0), bijective on t, and rows r, r + 2 of a transposed read differ in
+//   bit 1, so their two-chunk pairs do not collide.
+template <int D>
+__device__ __forceinline__ int sw2(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 1) | (((r >> 2) & 1) << 2) | ((r >> 3) & 1);
+}
 // Swizzle of tiles read by rows only (as the forward's K tiles).
-__device__ __forceinline__ int swr(int r) { return r & 15; }
+template <int D>
+__device__ __forceinline__ int swr(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
-// Direct loads of a 64-row tile of a row-major [rows, 128] BF16 matrix into
-// LDS: wave w fills the 1 KiB blocks 4 w .. 4 w + 3 (4 rows each); lane l
-// writes physical chunk l % 16 of its row with logical chunk (l % 16) ^ sw.
+// Direct loads of a 64-row tile of a row-major [rows, D] BF16 matrix into
+// LDS: wave w fills the 1 KiB blocks BPW w .. BPW w + BPW - 1; lane l writes
+// physical chunk l % CPR of its row with logical chunk (l % CPR) ^ sw.
 // Rows past `rows` read the last row (finite data the caller masks).
-template <bool SW2>
+template <int D, bool SW2>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int rows, uint4* dst, int wave, int lane) {
-  const int pc = lane & 15;
-  const uint32_t l0 = lds_addr(dst) + 4096u * (uint32_t)wave;
+  using C = BwdCfg<D>;
+  const int pc = lane % C::CPR;
+  const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(C::BPW * wave);
 #pragma unroll
-  for (int x = 0; x < 4; ++x) {
-    const int r = 16 * wave + 4 * x + (lane >> 4);
-    const int sw = SW2 ? sw2(r) : swr(r);
+  for (int x = 0; x < C::BPW; ++x) {
+    const int r = C::RPB * (C::BPW * wave + x) + lane / C::CPR;
+    const int sw = SW2 ? sw2<D>(r) : swr<D>(r);
     const int row = min(row0 + r, rows - 1);
-    dma16(src, 2u * (uint32_t)(row * kD + 8 * (pc ^ sw)), l0 + 1024u * x);
+    dma16(src, 2u * (uint32_t)(row * D + 8 * (pc ^ sw)), l0 + 1024u * x);
   }
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------- row pass
-// 16 lanes per row (8 columns each): delta = sum_t dO O in FP32, lse2 = lse
+// D / 8 lanes per row (8 columns each): delta = sum_t dO O in FP32, lse2 = lse
 // log2(e); rows N .. Npad - 1 of each head get zeros.
+template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
-  const size_t row = (size_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int c16 = threadIdx.x & 15;
+  constexpr int LPR = D / 8;
+  const size_t row = (size_t)blockIdx.x * (256 / LPR) + (threadIdx.x / LPR);
+  const int c16 = threadIdx.x % LPR;
   const size_t rows = (size_t)a.B * a.Hq * a.Npad;
   if (row >= rows) return;
   const size_t bh = row / a.Npad;
   const int n = (int)(row - bh * a.Npad);
   float s = 0.f;
   if (n < a.N) {
-    const size_t src = (bh * a.N + n) * kD + 8 * c16;
+    const size_t src = (bh * a.N + n) * D + 8 * c16;
     const uint4 x = *reinterpret_cast<const uint4*>(a.o + src);
     const uint4 y = *reinterpret_cast<const uint4*>(a.dout + src);
     s = bf16_lo(x.x) * bf16_lo(y.x) + bf16_hi(x.x) * bf16_hi(y.x) + bf16_lo(x.y) * bf16_lo(y.y) +
@@ -90,7 +108,7 @@ __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
         bf16_lo(x.w) * bf16_lo(y.w) + bf16_hi(x.w) * bf16_hi(y.w);
   }
 #pragma unroll
-  for (int m = 1; m < 16; m <<= 1) s += shfl_xor(s, m);
+  for (int m = 1; m < LPR; m <<= 1) s += shfl_xor(s, m);
   if (c16 == 0) {
     a.delta[row] = s;
     a.lse2[row] = n < a.N ? a.lse[bh * a.N + n] * kLog2e : 0.f;
@@ -98,11 +116,12 @@ __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
 }
 
 // ---------------------------------------------------------------- dK, dV
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
-  __shared__ uint4 q_lds[2][kTileChunks];
-  __shared__ uint4 do_lds[2][kTileChunks];
+  using C = BwdCfg<D>;
+  __shared__ uint4 q_lds[2][C::TILE_CHUNKS];
+  __shared__ uint4 do_lds[2][C::TILE_CHUNKS];
   __shared__ float4 st_lds[2][2][kBwdTile / 4];  // [buffer][lse2 | delta][rows / 4]
 
   const int tid = threadIdx.x;
@@ -122,16 +141,16 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   const int N = a.N;
   const int j0 = kb * kBwdKeyBlock;
   const int key = j0 + 16 * wave + j16;  // this lane's key (S columns, P^T rows)
-  const size_t kv_base = (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
+  const size_t kv_base = (size_t)(b * a.Hkv + hk) * (size_t)N * D;
 
   // K^T and V^T as B operands: lane holds row `key`, columns 32 kk + 8 b16 .. + 7.
-  bf16x8 kf[kKK16], vf[kKK16];
+  bf16x8 kf[C::KK16], vf[C::KK16];
   {
     const int kr = min(key, N - 1);
-    const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)kr * kD);
-    const uint4* vrow = reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)kr * kD);
+    const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)kr * D);
+    const uint4* vrow = reinterpret_cast<const uint4*>(a.v + kv_base + (size_t)kr * D);
 #pragma unroll
-    for (int kk = 0; kk < kKK16; ++kk) {
+    for (int kk = 0; kk < C::KK16; ++kk) {
       kf[kk] = __builtin_bit_cast(bf16x8, krow[4 * kk + b16]);
       vf[kk] = __builtin_bit_cast(bf16x8, vrow[4 * kk + b16]);
     }
@@ -148,8 +167,8 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     const int hq = hk * G + t / per_head;
     const int u = u_begin + t % per_head;
     const size_t rb = (size_t)(b * a.Hq + hq);
-    load_tile<true>(a.q + rb * N * kD, u * kBwdTile, N, q_lds[buf], wave, lane);
-    load_tile<true>(a.dout + rb * N * kD, u * kBwdTile, N, do_lds[buf], wave, lane);
+    load_tile<D, true>(a.q + rb * N * D, u * kBwdTile, N, q_lds[buf], wave, lane);
+    load_tile<D, true>(a.dout + rb * N * D, u * kBwdTile, N, do_lds[buf], wave, lane);
     if (wave == 0 && lane < 16) {  // lse2 and delta of the tile's 64 rows (256 B each)
       const size_t off = rb * a.Npad + (size_t)u * kBwdTile;
       dma16(a.lse2 + off, 16u * (uint32_t)lane, lds_addr(&st_lds[buf][0][0]));
@@ -158,23 +177,23 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   };
 
   // Per-lane LDS byte offsets. A fragments (rows): row 16 qt + j16, chunk 4 kk + b16.
-  int aoff[kKK16];
+  int aoff[C::KK16];
 #pragma unroll
-  for (int kk = 0; kk < kKK16; ++kk) aoff[kk] = 16 * (j16 * kCPR + ((4 * kk + b16) ^ sw2(j16)));
+  for (int kk = 0; kk < C::KK16; ++kk) aoff[kk] = 16 * (j16 * C::CPR + ((4 * kk + b16) ^ sw2<D>(j16)));
   // Transposed reads: lane names row 4 b16 + j16 / 4 (+ 32 u2, + 16 for the
   // second half) and 4 columns at 16 tt + 4 (j16 % 4); lane l receives column
   // 16 tt + j16 of rows 4 b16 .. 4 b16 + 3.
-  int troff[kTT];
+  int troff[C::TT];
   {
     const int r0 = 4 * b16 + (j16 >> 2);
 #pragma unroll
-    for (int tt = 0; tt < kTT; ++tt)
-      troff[tt] = 16 * (r0 * kCPR + ((2 * tt + ((j16 & 3) >> 1)) ^ sw2(r0))) + 8 * (j16 & 1);
+    for (int tt = 0; tt < C::TT; ++tt)
+      troff[tt] = 16 * (r0 * C::CPR + ((2 * tt + ((j16 & 3) >> 1)) ^ sw2<D>(r0))) + 8 * (j16 & 1);
   }
 
-  f32x4 dk[kTT], dv[kTT];
+  f32x4 dk[C::TT], dv[C::TT];
 #pragma unroll
-  for (int tt = 0; tt < kTT; ++tt) dk[tt] = dv[tt] = f32x4{};
+  for (int tt = 0; tt < C::TT; ++tt) dk[tt] = dv[tt] = f32x4{};
 
   const float c = a.c;
   issue(0, 0);  // n_t >= 1: the key block lies below N
@@ -195,9 +214,9 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
       s[qt] = f32x4{};
       dp[qt] = f32x4{};
 #pragma unroll
-      for (int kk = 0; kk < kKK16; ++kk) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * kCPR * 16);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * kCPR * 16);
+      for (int kk = 0; kk < C::KK16; ++kk) {
+        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * C::CPR * 16);
+        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * C::CPR * 16);
         s[qt] = mfma16(qa, kf[kk], s[qt]);
         dp[qt] = mfma16(da, vf[kk], dp[qt]);
       }
@@ -226,14 +245,14 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
                                     s[2 * u2 + 1][0], s[2 * u2 + 1][1], s[2 * u2 + 1][2], s[2 * u2 + 1][3]);
       const bf16x8 sa = pack_bf16x8(dp[2 * u2][0], dp[2 * u2][1], dp[2 * u2][2], dp[2 * u2][3],
                                     dp[2 * u2 + 1][0], dp[2 * u2 + 1][1], dp[2 * u2 + 1][2], dp[2 * u2 + 1][3]);
-      const int ro = u2 * 32 * kCPR * 16;
+      const int ro = u2 * 32 * C::CPR * 16;
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
+      for (int tt = 0; tt < C::TT; ++tt) {
         const i16x4 dlo = lds_read_tr(db + troff[tt] + ro);
-        const i16x4 dhi = lds_read_tr(db + troff[tt] + ro + 16 * kCPR * 16);
+        const i16x4 dhi = lds_read_tr(db + troff[tt] + ro + 16 * C::CPR * 16);
         dv[tt] = mfma16(pa, join_bf16x8(dlo, dhi), dv[tt]);
         const i16x4 qlo = lds_read_tr(qb + troff[tt] + ro);
-        const i16x4 qhi = lds_read_tr(qb + troff[tt] + ro + 16 * kCPR * 16);
+        const i16x4 qhi = lds_read_tr(qb + troff[tt] + ro + 16 * C::CPR * 16);
         dk[tt] = mfma16(sa, join_bf16x8(qlo, qhi), dk[tt]);
       }
     }
@@ -245,10 +264,10 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   for (int r = 0; r < 4; ++r) {
     const int kr = j0 + 16 * wave + 4 * b16 + r;
     if (kr < N) {
-      uint16_t* dkrow = a.dk + kv_base + (size_t)kr * kD;
-      uint16_t* dvrow = a.dv + kv_base + (size_t)kr * kD;
+      uint16_t* dkrow = a.dk + kv_base + (size_t)kr * D;
+      uint16_t* dvrow = a.dv + kv_base + (size_t)kr * D;
 #pragma unroll
-      for (int tt = 0; tt < kTT; ++tt) {
+      for (int tt = 0; tt < C::TT; ++tt) {
         dkrow[16 * tt + j16] = __builtin_bit_cast(uint16_t, (__bf16)(dk[tt][r] * sc));
         dvrow[16 * tt + j16] = __builtin_bit_cast(uint16_t, (__bf16)dv[tt][r]);
       }
@@ -257,11 +276,12 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
 }
 
 // ---------------------------------------------------------------- dQ
-template <bool CAUSAL>
+template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
-  __shared__ uint4 k_lds[2][kTileChunks];
-  __shared__ uint4 v_lds[2][kTileChunks];
+  using C = BwdCfg<D>;
+  __shared__ uint4 k_lds[2][C::TILE_CHUNKS];
+  __shared__ uint4 v_lds[2][C::TILE_CHUNKS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -279,23 +299,23 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const int N = a.N;
   const int q0 = qb * kBwdRowBlock;
   const int qi = q0 + 32 * wave + li;
-  const size_t q_base = (size_t)(b * a.Hq + h) * (size_t)N * kD;
-  const uint16_t* kg = a.k + (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
-  const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * kD;
+  const size_t q_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
+  const uint16_t* kg = a.k + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
+  const uint16_t* vg = a.v + (size_t)(b * a.Hkv + hk) * (size_t)N * D;
   const int kv_end = CAUSAL ? min(N, q0 + kBwdRowBlock) : N;
   const int n_tiles = (kv_end + kBwdTile - 1) / kBwdTile;
 
-  load_tile<true>(kg, 0, N, k_lds[0], wave, lane);
-  load_tile<false>(vg, 0, N, v_lds[0], wave, lane);
+  load_tile<D, true>(kg, 0, N, k_lds[0], wave, lane);
+  load_tile<D, false>(vg, 0, N, v_lds[0], wave, lane);
 
   // Q^T and dO^T as B operands (lane = query row qi), lse2 and delta of qi.
-  bf16x8 qf[kKK32], df[kKK32];
+  bf16x8 qf[C::KK32], df[C::KK32];
   {
-    const size_t r = q_base + (size_t)(qi < N ? qi : 0) * kD;
+    const size_t r = q_base + (size_t)(qi < N ? qi : 0) * D;
     const uint4* qrow = reinterpret_cast<const uint4*>(a.q + r);
     const uint4* drow = reinterpret_cast<const uint4*>(a.dout + r);
 #pragma unroll
-    for (int kk = 0; kk < kKK32; ++kk) {
+    for (int kk = 0; kk < C::KK32; ++kk) {
       qf[kk] = __builtin_bit_cast(bf16x8, qrow[2 * kk + g]);
       df[kk] = __builtin_bit_cast(bf16x8, drow[2 * kk + g]);
     }
@@ -305,11 +325,11 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const float dl = a.delta[st];
 
   // LDS offsets. K rows (sw2) and V rows (swr): row li, chunk 2 kk + g.
-  int koff[kKK32], voff[kKK32];
+  int koff[C::KK32], voff[C::KK32];
 #pragma unroll
-  for (int kk = 0; kk < kKK32; ++kk) {
-    koff[kk] = 16 * (li * kCPR + ((2 * kk + g) ^ sw2(li)));
-    voff[kk] = 16 * (li * kCPR + ((2 * kk + g) ^ swr(li)));
+  for (int kk = 0; kk < C::KK32; ++kk) {
+    koff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ sw2<D>(li)));
+    voff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ swr<D>(li)));
   }
   // K^T transposed reads (as the forward's V^T): lane t16 names row
   // 4 g + t16 / 4 (+ 32 jt + 16 hh, + 8 for the upper 4 keys) and 4 columns at
@@ -317,17 +337,17 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const int t16 = lane & 15;
   const int vch = (lane >> 4) & 1;
   const int vrow = 4 * g + (t16 >> 2);
-  int klo[kDT], khi[kDT];
+  int klo[C::DT], khi[C::DT];
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) {
+  for (int dt = 0; dt < C::DT; ++dt) {
     const int chunk = (32 * dt + 16 * vch + 4 * (t16 & 3)) >> 3;
-    klo[dt] = 16 * (vrow * kCPR + (chunk ^ sw2(vrow))) + 8 * (t16 & 1);
-    khi[dt] = 16 * ((vrow + 8) * kCPR + (chunk ^ sw2(vrow + 8))) + 8 * (t16 & 1);
+    klo[dt] = 16 * (vrow * C::CPR + (chunk ^ sw2<D>(vrow))) + 8 * (t16 & 1);
+    khi[dt] = 16 * ((vrow + 8) * C::CPR + (chunk ^ sw2<D>(vrow + 8))) + 8 * (t16 & 1);
   }
 
-  f32x16 dq[kDT];
+  f32x16 dq[C::DT];
 #pragma unroll
-  for (int dt = 0; dt < kDT; ++dt) dq[dt] = f32x16{};
+  for (int dt = 0; dt < C::DT; ++dt) dq[dt] = f32x16{};
   const float c = a.c;
 
   for (int t = 0; t < n_tiles; ++t) {
@@ -335,8 +355,8 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (t + 1 < n_tiles) {
-      load_tile<true>(kg, (t + 1) * kBwdTile, N, k_lds[buf ^ 1], wave, lane);
-      load_tile<false>(vg, (t + 1) * kBwdTile, N, v_lds[buf ^ 1], wave, lane);
+      load_tile<D, true>(kg, (t + 1) * kBwdTile, N, k_lds[buf ^ 1], wave, lane);
+      load_tile<D, false>(vg, (t + 1) * kBwdTile, N, v_lds[buf ^ 1], wave, lane);
     }
     const int kv0 = t * kBwdTile;
     const char* kb = reinterpret_cast<const char*>(k_lds[buf]);
@@ -345,11 +365,11 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
     // S^T = K Q^T and dP^T = V dO^T for two 32-key halves.
     f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < kKK32; ++kk) {
+    for (int kk = 0; kk < C::KK32; ++kk) {
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * kCPR * 16);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
       const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vb + voff[kk]);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vb + voff[kk] + 32 * kCPR * 16);
+      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vb + voff[kk] + 32 * C::CPR * 16);
       s0 = mfma32(k0, qf[kk], s0);
       s1 = mfma32(k1, qf[kk], s1);
       p0 = mfma32(v0, df[kk], p0);
@@ -380,9 +400,9 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int ro = (32 * jt + 16 * hh) * kCPR * 16;
+        const int ro = (32 * jt + 16 * hh) * C::CPR * 16;
 #pragma unroll
-        for (int dt = 0; dt < kDT; ++dt) {
+        for (int dt = 0; dt < C::DT; ++dt) {
           const i16x4 lo = lds_read_tr(kb + klo[dt] + ro);
           const i16x4 hi = lds_read_tr(kb + khi[dt] + ro);
           dq[dt] = mfma32(join_bf16x8(lo, hi), sb[jt][hh], dq[dt]);
@@ -392,10 +412,10 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
 
   // Epilogue: lane holds row qi, columns 32 dt + 8 rq + 4 g + (0..3).
   if (qi < N) {
-    uint16_t* row = a.dq + q_base + (size_t)qi * kD;
+    uint16_t* row = a.dq + q_base + (size_t)qi * D;
     const float sc = a.scale;
 #pragma unroll
-    for (int dt = 0; dt < kDT; ++dt)
+    for (int dt = 0; dt < C::DT; ++dt)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq)
         *reinterpret_cast<uint2*>(row + 32 * dt + 8 * rq + 4 * g) =
@@ -404,23 +424,29 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   }
 }
 
-hipError_t launch_bwd(const BwdArgs& a, bool causal, hipStream_t stream) {
+template <int D>
+static hipError_t launch_bwd_d(const BwdArgs& a, bool causal, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Hq * a.Npad;
-  hipLaunchKernelGGL(fa_bwd_rows_kernel, dim3((unsigned)((rows + 15) / 16)), dim3(256), 0, stream, a);
+  const size_t per_wg = 256 / (D / 8);
+  hipLaunchKernelGGL(fa_bwd_rows_kernel<D>, dim3((unsigned)((rows + per_wg - 1) / per_wg)), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nwg_kv = a.B * a.Hkv * a.nkb;
   const int nwg_q = a.B * a.Hq * a.nqb;
   if (causal) {
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<true>, dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, true>), dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<true>, dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, true>), dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
   } else {
-    hipLaunchKernelGGL(fa_bwd_dkdv_kernel<false>, dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<D, false>), dim3(nwg_kv), dim3(256), 0, stream, a, nwg_kv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(fa_bwd_dq_kernel<false>, dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<D, false>), dim3(nwg_q), dim3(256), 0, stream, a, nwg_q);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t stream) {
+  return d == 128 ? launch_bwd_d<128>(a, causal, stream) : launch_bwd_d<64>(a, causal, stream);
 }
 
 }  // namespace fa

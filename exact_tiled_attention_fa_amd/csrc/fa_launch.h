@@ -55,7 +55,7 @@ hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t stream);
 // Merge the key-split partials of a split forward into O (BF16) and lse.
 hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 
-// Backward pass (d = 128): a row pass (lse2 = lse log2 e and delta = rowsum(dO O),
+// Backward pass (d = 64 or 128): a row pass (lse2 = lse log2 e and delta = rowsum(dO O),
 // both padded to Npad rows with zeros), then dK/dV with one work-group per
 // (batch, KV head, 64-key block) sweeping the query tiles of every query head
 // of its group, and dQ with one work-group per (batch, query head, 128-row
@@ -83,7 +83,7 @@ constexpr int kBwdKeyBlock = 64;
 constexpr int kBwdRowBlock = 128;
 constexpr int kBwdTile = 64;  // rows per Q/dO tile (dK/dV) and per K/V tile (dQ)
 
-hipError_t launch_bwd(const BwdArgs& a, bool causal, hipStream_t stream);
+hipError_t launch_bwd(const BwdArgs& a, int d, bool causal, hipStream_t stream);
 
 // Split-KV decode: one work-group per (batch, KV head, head group, chunk).
 struct DecArgs {

@@ -48,7 +48,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or num_splits out of range */
-  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 (fa_bwd, fa_fwd_fp8: not 128) */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 (fa_fwd_fp8: not 128) */
   FA_ERR_GQA = -4,       /* Hq is not a multiple of Hkv */
   FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
@@ -197,7 +197,7 @@ size_t fa_bwd_workspace_bytes(int B, int Hq, int N, int d);
  *
  *   q, o, dout, dq [B, Hq,  N, d] bf16;  k, v, dk, dv [B, Hkv, N, d] bf16
  *   lse            [B, Hq,  N]    fp32, natural log, as fa_fwd wrote it
- *   d = 128 only (FA_ERR_HEAD_DIM otherwise).
+ *   d = 64 or 128 (FA_ERR_HEAD_DIM otherwise).
  *   workspace: device, 16-byte aligned, at least fa_bwd_workspace_bytes(B, Hq,
  *   N, d) bytes, owned by the caller; contents on entry are ignored. Calls
  *   sharing a workspace must be ordered.

@@ -123,7 +123,7 @@ def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1
 
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(o=None), -1), (dict(do=None), -1), (dict(dk=None), -1), (dict(lse=None), -1),
-    (dict(N=0), -2), (dict(B=-1), -2), (dict(d=64), -3), (dict(d=96), -3), (dict(Hq=3, Hkv=2), -4),
+    (dict(N=0), -2), (dict(B=-1), -2), (dict(d=256), -3), (dict(d=96), -3), (dict(Hq=3, Hkv=2), -4),
     (dict(dv=BAD), -5), (dict(do=BAD), -5), (dict(ws=BAD), -5), (dict(causal=3), -8),
     (dict(scale=float("nan")), -8), (dict(ws=None), -6), (dict(wsb=64), -6),
 ])
@@ -134,7 +134,8 @@ def test_bwd_rejects(lib, kw, status):
 def test_bwd_workspace_size(lib):
     # two floats per row, rows padded to 64 per head
     assert lib.fa_bwd_workspace_bytes(1, 2, 300, 128) == (2 * 2 * 320 * 4 + 255) // 256 * 256
-    assert lib.fa_bwd_workspace_bytes(1, 2, 300, 64) == 0
+    assert lib.fa_bwd_workspace_bytes(1, 2, 300, 64) == (2 * 2 * 320 * 4 + 255) // 256 * 256
+    assert lib.fa_bwd_workspace_bytes(1, 2, 300, 96) == 0
     assert lib.fa_bwd_workspace_bytes(0, 2, 300, 128) == 0
 
 

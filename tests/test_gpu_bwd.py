@@ -28,19 +28,19 @@ def _gpu_bwd(qb, kb, vb, gb, causal, scale):
     return to_f64(dq), to_f64(dk), to_f64(dv)
 
 
-def _inputs(B, Hq, Hkv, N, seed):
-    case = si.FwdCase(f"bwd {B}x{Hq}/{Hkv}x{N}", B, Hq, Hkv, N, 128, False, seed)
+def _inputs(B, Hq, Hkv, N, seed, d=128):
+    case = si.FwdCase(f"bwd {B}x{Hq}/{Hkv}x{N}", B, Hq, Hkv, N, d, False, seed)
     qb, kb, vb = si.fwd_inputs(case)
-    gb = si.normal_bf16(np.random.default_rng(seed + 10_000), (B, Hq, N, 128))
+    gb = si.normal_bf16(np.random.default_rng(seed + 10_000), (B, Hq, N, d))
     return qb, kb, vb, gb
 
 
-def _run_small(B, Hq, Hkv, N, causal, seed, scale=None):
-    scale = 128 ** -0.5 if scale is None else scale
-    what = f"bwd B{B} Hq{Hq} Hkv{Hkv} N{N} causal={causal} scale={scale:.4g}"
+def _run_small(B, Hq, Hkv, N, causal, seed, scale=None, d=128):
+    scale = d ** -0.5 if scale is None else scale
+    what = f"bwd B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal} scale={scale:.4g}"
     print(f"[bwd] {what} seed={seed}", flush=True)
     sys.stdout.flush()
-    qb, kb, vb, gb = _inputs(B, Hq, Hkv, N, seed)
+    qb, kb, vb, gb = _inputs(B, Hq, Hkv, N, seed, d)
     dq, dk, dv = _gpu_bwd(qb, kb, vb, gb, causal, scale)
     qf, kf, vf, gf = (si.bf16_bits_to_f32(x).astype(np.float64) for x in (qb, kb, vb, gb))
     rq, rk, rv = fa_oracle.attention_bwd_ref(qf, kf, vf, gf, causal, scale)
@@ -59,6 +59,18 @@ def test_bwd_small(B, Hq, Hkv, N, causal):
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.3])
 def test_bwd_scale_edge_cases(scale):
     _run_small(1, 2, 1, 300, True, seed=800, scale=scale)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 2, 2, 256), (2, 4, 2, 200), (1, 1, 1, 1), (1, 3, 1, 67),
+                                        (1, 2, 1, 1000)])
+def test_bwd_small_d64(B, Hq, Hkv, N, causal):
+    _run_small(B, Hq, Hkv, N, causal, seed=900 + N + Hq, d=64)
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.2])
+def test_bwd_scale_edge_cases_d64(scale):
+    _run_small(1, 2, 1, 300, True, seed=950, scale=scale, d=64)
 
 
 @pytest.mark.parametrize("causal", [False, True])
