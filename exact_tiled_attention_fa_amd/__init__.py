@@ -94,7 +94,7 @@ def _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale):
 def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k_scale: float, v_scale: float,
             causal: bool = False, scale: float | None = None, out: torch.Tensor | None = None,
             lse: torch.Tensor | None = None):
-    """FP8 attention forward (d = 128): q [B,Hq,N,d], k/v [B,Hkv,N,d] of OCP E4M3 codes
+    """FP8 attention forward (d = 64 or 128): q [B,Hq,N,d], k/v [B,Hkv,N,d] of OCP E4M3 codes
     (torch.float8_e4m3fn or uint8) whose values are q_scale*q, k_scale*k, v_scale*v
     -> (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32)."""
     B, Hq, N, _ = q.shape

@@ -62,7 +62,7 @@ extern "C" const char* fa_status_string(int status) {
     case FA_OK: return "FA_OK";
     case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
     case FA_ERR_SHAPE: return "FA_ERR_SHAPE: a size is out of range";
-    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128 (128 for fa_fwd_fp8)";
+    case FA_ERR_HEAD_DIM: return "FA_ERR_HEAD_DIM: d must be 64 or 128";
     case FA_ERR_GQA: return "FA_ERR_GQA: Hq must be a multiple of Hkv";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: tensors must be 16-byte aligned (lse 4-byte)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
@@ -201,7 +201,6 @@ int check_fp8_args(const void* q, const void* k, const void* v, float q_scale, f
                    void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale) {
   int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
-  if (d != 128) return FA_ERR_HEAD_DIM;
   if (!isfinite(q_scale) || !isfinite(k_scale) || !isfinite(v_scale) ||
       !isfinite((double)scale * q_scale * k_scale * fa::kLog2eHost) ||
       !isfinite((float)((double)scale * q_scale * k_scale * fa::kLog2eHost)))
@@ -211,7 +210,7 @@ int check_fp8_args(const void* q, const void* k, const void* v, float q_scale, f
 
 int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const void* v, float q_scale,
                            float k_scale, float v_scale, void* o, float* lse, int B, int Hq, int Hkv, int N,
-                           int causal, float scale, void* ws, hipStream_t s) {
+                           int d, int causal, float scale, void* ws, hipStream_t s) {
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);  // E4M3 bytes; the kernel reads them as such
   a.k = static_cast<const uint16_t*>(k);
@@ -226,10 +225,10 @@ int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
   a.o_part = static_cast<uint16_t*>(ws);
-  a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * 128) : nullptr;
+  a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = v_scale;
-  hipError_t e = fa::launch_fwd_fp8(a, causal != 0, s);
-  if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, 128, causal != 0, s);
+  hipError_t e = fa::launch_fwd_fp8(a, d, causal != 0, s);
+  if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, d, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }
 
@@ -246,7 +245,7 @@ extern "C" int fa_fwd_fp8_ws(const void* q, const void* k, const void* v, float 
     if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
   }
-  return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale,
+  return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale,
                                 p.ws_bytes > 0 ? workspace : nullptr, reinterpret_cast<hipStream_t>(stream));
 }
 
@@ -258,11 +257,11 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_s
   const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.ws_bytes == 0)
-    return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale,
+    return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale,
                                   nullptr, s);
   void* ws = nullptr;
   if (hipMallocAsync(&ws, p.ws_bytes, s) != hipSuccess || !ws) return FA_ERR_LAUNCH;
-  st = launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, causal, scale, ws, s);
+  st = launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, s);
   const hipError_t ef = hipFreeAsync(ws, s);
   return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
 }

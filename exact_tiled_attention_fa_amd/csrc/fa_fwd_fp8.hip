@@ -51,38 +51,70 @@ __device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
-constexpr int kD8 = 128;              // head dimension (bytes per K/V row)
-constexpr int kChunks8 = kD8 / 16;    // 16-byte chunks per row
-constexpr int kTile8 = kFwdKeys * kD8;  // bytes per K or V tile
 constexpr float kRescaleSlack8 = 2.f;
 constexpr float kPBias8 = 6.f;        // p = 2^(t - m + kPBias8) <= 2^8
 
-// LDS chunk swizzles (16-byte chunk index within a 128-byte row).
-// K: chunk ^ ((r >> 1) & 7) keeps a 16-lane fragment read (16 rows, one chunk
-// column) on 16 distinct 16-byte bank groups.
-__device__ __forceinline__ int kswz8(int r) { return (r >> 1) & 7; }
-// V: column chunk c is stored at ((c & 1) << 2 | c >> 1) ^ f(r) with f taking
-// bits 1 and 3 of the key: the transposed reads of one 16-lane block (8 keys
-// x two 8-byte halves) and of its partner block (the next 16 columns) then
-// cover 32 distinct 8-byte bank slots.
+template <int D>
+struct Fp8Cfg {
+  static constexpr int CH = D / 16;             // 16-byte chunks per K/V row (D bytes)
+  static constexpr int TILE = kFwdKeys * D;     // bytes per K or V tile
+  static constexpr int KK = D / 64;             // k-steps of S^T = K Q^T
+  static constexpr int DT = D / 32;             // 32-wide d tiles of O^T
+  static constexpr int BLOCKS = TILE / 1024;    // 1 KiB direct-load blocks per tile
+  static constexpr int RPB = 1024 / D;          // rows per block
+};
+
+// LDS chunk swizzles (16-byte chunk index within a D-byte row).
+// K (fragment reads: 16 consecutive rows at one chunk column): D = 128 has
+// 128-byte rows, two per 64 banks, so chunk ^ ((r >> 1) & 7); D = 64 has
+// four rows per 64 banks, so chunk ^ ((r >> 2) & 3). Either way the 16 rows
+// land on 16 distinct 16-byte bank slots.
+template <int D>
+__device__ __forceinline__ int kswz8(int r) { return D == 128 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+// V (transposed reads: one 16-lane block takes 8 keys x two 8-byte halves of
+// one chunk column, its partner block the next chunk column).
+//   D = 128: column chunk c is stored at ((c & 1) << 2 | c >> 1) ^ f(r), f
+//   taking bits 1 and 3 of the key, so the two blocks cover 32 distinct
+//   8-byte slots.
+//   D = 64: chunk c is stored at c ^ (2 * bit 3 of the key): the 8 keys of a
+//   block (two runs of 4 consecutive keys, 8 apart) fill 8 distinct 16-byte
+//   slots and the partner block's column the other 8.
 __device__ __forceinline__ int vf8(int r) { return ((r >> 1) & 1) | ((r >> 2) & 2); }
-__device__ __forceinline__ int vphys8(int c, int r) { return (((c & 1) << 2) | (c >> 1)) ^ vf8(r); }
-__device__ __forceinline__ int vlogical8(int p, int r) {
-  const int x = p ^ vf8(r);
-  return ((x & 3) << 1) | (x >> 2);
+template <int D>
+__device__ __forceinline__ int vphys8(int c, int r) {
+  if (D == 128) return (((c & 1) << 2) | (c >> 1)) ^ vf8(r);
+  return c ^ (((r >> 3) & 1) << 1);
 }
+template <int D>
+__device__ __forceinline__ int vlogical8(int p, int r) {
+  if (D == 128) {
+    const int x = p ^ vf8(r);
+    return ((x & 3) << 1) | (x >> 2);
+  }
+  return p ^ (((r >> 3) & 1) << 1);
+}
+// BF16 staging of the output rows: 8-byte unit e of row r is stored at unit
+// e ^ ostw(r) (as the BF16 pass).
+template <int D>
+__device__ __forceinline__ int ostw(int r) { return D == 128 ? r : ((r >> 1) & 15); }
 
 }  // namespace
 
-template <bool CAUSAL, int W>
+template <int D, bool CAUSAL, int W>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void fa_fwd_fp8_kernel(FwdArgs a) {
+  using C = Fp8Cfg<D>;
   constexpr int ROWS = kFwdWaveRows * W;
-  constexpr int BPW = kTile8 / 1024 / W;  // 1 KiB direct-load blocks per wave per tile
-  constexpr int RPB = 1024 / kD8;         // rows per block
-  constexpr int DT = kD8 / 32;            // 32-wide d tiles of O^T
-  // K buffers 0, 1 then V buffers 0, 1 (8 KiB each); after the sweep the
-  // epilogue stages each wave's 32 BF16 rows (8 KiB) over the whole array.
+  // 1 KiB direct-load blocks per wave per tile; with fewer blocks than waves
+  // (d = 64, 8 waves) the first C::BLOCKS waves load one each.
+  constexpr int BPW = C::BLOCKS >= W ? C::BLOCKS / W : 1;
+  constexpr int RPB = C::RPB;
+  constexpr int DT = C::DT;
+  constexpr int kD8 = D;
+  constexpr int kTile8 = C::TILE;
+  constexpr int kChunks8 = C::CH;
+  // K buffers 0, 1 then V buffers 0, 1; after the sweep the epilogue stages
+  // each wave's 32 BF16 rows over the whole array.
   constexpr int STAGE_BYTES = W * 32 * kD8 * 2 > 4 * kTile8 ? W * 32 * kD8 * 2 : 4 * kTile8;
   __shared__ uint4 smem[STAGE_BYTES / 16];
   char* const lds = reinterpret_cast<char*>(smem);
@@ -130,13 +162,14 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int x = 0; x < BPW; ++x) {
     const int r = (wave * BPW + x) * RPB + dma_row;
-    kdo[x] = (uint32_t)(r * kD8 + 16 * (dma_p ^ kswz8(r)));
-    vdo[x] = (uint32_t)(r * kD8 + 16 * vlogical8(dma_p, r));
+    kdo[x] = (uint32_t)(r * kD8 + 16 * (dma_p ^ kswz8<D>(r)));
+    vdo[x] = (uint32_t)(r * kD8 + 16 * vlogical8<D>(dma_p, r));
   }
   auto issue = [&](const uint8_t* src, const uint32_t* offs, bool is_v, int tile, char* dst) {
     const uint8_t* base = src + (size_t)tile * kTile8;
     const int rows = n_keys - tile * kFwdKeys;
     const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(wave * BPW);
+    if (C::BLOCKS < W && wave >= C::BLOCKS) return;
     if (rows >= kFwdKeys) {
 #pragma unroll
       for (int x = 0; x < BPW; ++x) dma16(base, offs[x], l0 + 1024u * x);
@@ -144,7 +177,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
       for (int x = 0; x < BPW; ++x) {
         const int r = (wave * BPW + x) * RPB + dma_row;
-        const int lc = is_v ? vlogical8(dma_p, r) : (dma_p ^ kswz8(r));
+        const int lc = is_v ? vlogical8<D>(dma_p, r) : (dma_p ^ kswz8<D>(r));
         dma16(base, (uint32_t)(min(r, rows - 1) * kD8 + 16 * lc), l0 + 1024u * x);
       }
     }
@@ -159,11 +192,11 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   const int qi = q0 + wave * 32 + li;
   const int sign = a.c < 0.f ? (int)0x80808080u : 0;
   const float c = fmaxf(fabsf(a.c), 1.17549435e-38f);
-  i32x8 qf[2];
+  i32x8 qf[C::KK];
   {
     const uint4* qrow = reinterpret_cast<const uint4*>(q8 + ((size_t)(b * a.Hq + h) * N + (qi < N ? qi : 0)) * kD8);
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < C::KK; ++kk) {
       uint4 w0 = qi < N ? qrow[4 * kk + 2 * g] : make_uint4(0u, 0u, 0u, 0u);
       uint4 w1 = qi < N ? qrow[4 * kk + 2 * g + 1] : make_uint4(0u, 0u, 0u, 0u);
       qf[kk] = i32x8{(int)w0.x ^ sign, (int)w0.y ^ sign, (int)w0.z ^ sign, (int)w0.w ^ sign,
@@ -175,18 +208,18 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   // (rows 32 + li add 4 KiB). V^T: as a source lane, lane i of 16-lane block
   // beta names the run of key 8 (e / 4) + 4 g + e % 4 (e = i / 2; + 16 n for
   // read n) at column 32 dt + 16 (beta % 2) + 8 (i % 2).
-  int koff[2][2];
+  int koff[C::KK][2];
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) koff[kk][hh] = li * kD8 + 16 * ((4 * kk + 2 * g + hh) ^ kswz8(li));
+    for (int hh = 0; hh < 2; ++hh) koff[kk][hh] = li * kD8 + 16 * ((4 * kk + 2 * g + hh) ^ kswz8<D>(li));
   const int i16 = lane & 15;
   const int beta2 = (lane >> 4) & 1;
   const int e8 = i16 >> 1;
   const int vkey = 8 * (e8 >> 2) + 4 * g + (e8 & 3);
   int voff[DT];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) voff[dt] = vkey * kD8 + 16 * vphys8(2 * dt + beta2, vkey) + 8 * (i16 & 1);
+  for (int dt = 0; dt < DT; ++dt) voff[dt] = vkey * kD8 + 16 * vphys8<D>(2 * dt + beta2, vkey) + 8 * (i16 & 1);
 
   float m_run = -INFINITY;
   float l_run = 0.f;  // running sum of 2^(t - m_run + kPBias8)
@@ -200,7 +233,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < C::KK; ++kk) {
       const uint4 a0 = *reinterpret_cast<const uint4*>(kb + koff[kk][0]);
       const uint4 a1 = *reinterpret_cast<const uint4*>(kb + koff[kk][1]);
       const uint4 b0 = *reinterpret_cast<const uint4*>(kb + koff[kk][0] + 32 * kD8);
@@ -212,10 +245,10 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2 * C::KK; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (i < 2) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      if (valu) __builtin_amdgcn_sched_group_barrier(0x002, 12, 0);
+      if (i + 2 < 2 * C::KK) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      if (valu) __builtin_amdgcn_sched_group_barrier(0x002, 24 / C::KK, 0);
     }
   };
 
@@ -365,7 +398,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
     for (int rq = 0; rq < 4; ++rq) {
       const int e = 8 * dt + 2 * rq + g;
-      *reinterpret_cast<uint2*>(stage + li * (kD8 * 2) + 8 * (e ^ li)) =
+      *reinterpret_cast<uint2*>(stage + li * (kD8 * 2) + 8 * (e ^ ostw<D>(li))) =
           pack_bf16x4(oacc[dt][4 * rq + 0] * inv, oacc[dt][4 * rq + 1] * inv,
                       oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
     }
@@ -378,22 +411,29 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + lane / C16;
-    uint4 w = *reinterpret_cast<const uint4*>(stage + r * (kD8 * 2) + 16 * (c16 ^ (r >> 1)));
-    if (r & 1) w = make_uint4(w.z, w.w, w.x, w.y);
+    const int sw = ostw<D>(r);
+    uint4 w = *reinterpret_cast<const uint4*>(stage + r * (kD8 * 2) + 16 * (c16 ^ (sw >> 1)));
+    if (sw & 1) w = make_uint4(w.z, w.w, w.x, w.y);
     const int row = q0 + wave * 32 + r;
     if (row < N) *reinterpret_cast<uint4*>(dst + (size_t)row * row_stride + 8 * c16) = w;
   }
 }
 
-template <bool CAUSAL, int W>
+template <int D, bool CAUSAL, int W>
 static hipError_t launch_fp8_t(const FwdArgs& a, hipStream_t stream) {
-  hipLaunchKernelGGL((fa_fwd_fp8_kernel<CAUSAL, W>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
+  hipLaunchKernelGGL((fa_fwd_fp8_kernel<D, CAUSAL, W>), dim3(a.nwg), dim3(64 * W), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t stream) {
-  if (a.rows == kFwdWaveRows * 8) return causal ? launch_fp8_t<true, 8>(a, stream) : launch_fp8_t<false, 8>(a, stream);
-  return causal ? launch_fp8_t<true, 4>(a, stream) : launch_fp8_t<false, 4>(a, stream);
+template <int D>
+static hipError_t launch_fp8_d(const FwdArgs& a, bool causal, hipStream_t stream) {
+  if (a.rows == kFwdWaveRows * 8)
+    return causal ? launch_fp8_t<D, true, 8>(a, stream) : launch_fp8_t<D, false, 8>(a, stream);
+  return causal ? launch_fp8_t<D, true, 4>(a, stream) : launch_fp8_t<D, false, 4>(a, stream);
+}
+
+hipError_t launch_fwd_fp8(const FwdArgs& a, int d, bool causal, hipStream_t stream) {
+  return d == 128 ? launch_fp8_d<128>(a, causal, stream) : launch_fp8_d<64>(a, causal, stream);
 }
 
 }  // namespace fa

@@ -50,8 +50,8 @@ inline int fwd_waves(bool causal, int N, int64_t blocks256, int cus) {
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream);
-// FP8 E4M3 inputs (q, k, v point at bytes), d = 128; c folds scale * q_scale * k_scale.
-hipError_t launch_fwd_fp8(const FwdArgs& a, bool causal, hipStream_t stream);
+// FP8 E4M3 inputs (q, k, v point at bytes), d = 64 or 128; c folds scale * q_scale * k_scale.
+hipError_t launch_fwd_fp8(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 // Merge the key-split partials of a split forward into O (BF16) and lse.
 hipError_t launch_fwd_combine(const FwdArgs& a, int d, bool causal, hipStream_t stream);
 

@@ -48,7 +48,7 @@ typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
   FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or num_splits out of range */
-  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 (fa_fwd_fp8: not 128) */
+  FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
   FA_ERR_GQA = -4,       /* Hq is not a multiple of Hkv */
   FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
@@ -112,13 +112,13 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
  *   o   [B, Hq,  N, d] bf16   output, rounded to nearest even
  *   lse [B, Hq,  N]    fp32   natural-log logsumexp of scale * q.k (dequantised)
  *
- * d must be 128 (FA_ERR_HEAD_DIM otherwise). q_scale, k_scale, v_scale and
+ * d must be 64 or 128 (FA_ERR_HEAD_DIM otherwise). q_scale, k_scale, v_scale and
  * scale * q_scale * k_scale must be finite (FA_ERR_ARG otherwise); any sign.
  * Arithmetic: Q.K products exact, accumulated by the FP8 matrix cores; the
  * weights 2^(t - m + 6) are rounded to E4M3 (relative error <= 2^-4) for the
  * P V product while the row sums use their FP32 values; O and lse otherwise
  * as fa_fwd. Key splits, their temporary buffer and the errors are those of
- * fa_fwd (the workspace size is fa_fwd_workspace_bytes(B, Hq, N, 128)).
+ * fa_fwd (the workspace size is fa_fwd_workspace_bytes(B, Hq, N, d)).
  */
 int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_scale, float k_scale, float v_scale,
                void* o, float* lse, int B, int Hq, int Hkv, int N, int d, int causal, float scale,

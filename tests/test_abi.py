@@ -164,7 +164,7 @@ def fwd_fp8(lib, q=P, k=P, v=P, qs=0.01, ks=0.01, vs=0.01, o=P, lse=P, B=1, Hq=1
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), -1), (dict(v=None), -1), (dict(o=None), -1),
     (dict(B=0), -2), (dict(N=-1), -2),
-    (dict(d=64), -3), (dict(d=96), -3),
+    (dict(d=96), -3), (dict(d=256), -3), (dict(d=0), -3),
     (dict(Hq=5, Hkv=2), -4),
     (dict(k=BAD), -5), (dict(lse=P + 1), -5),
     (dict(causal=3), -8), (dict(scale=float("nan")), -8),
@@ -185,7 +185,7 @@ def test_fwd_fp8_ws_rejects(lib):
         return lib.fa_fwd_fp8_ws(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"],
                                  a["Hq"], a["Hkv"], a["N"], a["d"], a["causal"], a["scale"], P, 0, None)
     assert call(q=None) == -1
-    assert call(d=64) == -3
+    assert call(d=96) == -3
     assert call(vs=float("nan")) == -8
 
 

@@ -81,12 +81,12 @@ def _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p, split):
     return out
 
 
-def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0):
+def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0, d=128):
     import torch
     import exact_tiled_attention_fa_amd as fa
-    case = si.FwdCase(name, B, Hq, Hkv, N, 128, causal, seed)
+    case = si.FwdCase(name, B, Hq, Hkv, N, d, causal, seed)
     scale = case.scale if scale is None else scale
-    _say(f"[fp8] {name} B{B} Hq{Hq} Hkv{Hkv} N{N} causal={causal} seed={seed} scale={scale}")
+    _say(f"[fp8] {name} B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal} seed={seed} scale={scale}")
     q8, k8, v8, qs, ks, vs = si.fwd_fp8_inputs(case)
     qs *= q_sign
     q, k, v = _upload(q8), _upload(k8), _upload(v8)
@@ -102,7 +102,7 @@ def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0
         lse_np = np.stack([lse_np[:, h, rows[h]] for h in range(Hq)], axis=1)
     o_ref, lse_ref, p = fa_oracle.attention_fp8_ref(q8, k8, v8, qs, ks, vs, causal, scale, rows=rows,
                                                     return_p=True)
-    split = fa.fwd_workspace_bytes(B, Hq, N, 128) > 0
+    split = fa.fwd_workspace_bytes(B, Hq, N, d) > 0
     bound = _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p, split)
     del p
     full = bound + 0.5 * ulp_bf16(np.abs(o_ref) * (1 + 2.0 ** -7)) + 1e-6
@@ -149,3 +149,20 @@ def test_fp8_scale_edges(scale, q_sign):
 def test_fp8_32_heads_4k(causal):
     """The 32-head N=4096 workload shape, 96 sampled rows per head."""
     _run("1x32x4096 d128", 1, 32, 32, 4096, causal, seed=3, sampled=96)
+
+
+@pytest.mark.parametrize("N", [1, 63, 100, 129, 1000])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_d64_ragged(N, causal):
+    _run(f"d64 ragged N{N}", 2, 4, 2, N, causal, seed=3400 + N, d=64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_d64_key_split_gqa(causal):
+    """d = 64 with grouped keys on one batch of 2 query heads: the keys split."""
+    _run("d64 split 1x2x2048", 1, 2, 1, 2048, causal, seed=3501, d=64)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_d64_32_heads_4k(causal):
+    _run("1x32x4096 d64", 1, 32, 32, 4096, causal, seed=4, sampled=96, d=64)
