@@ -294,21 +294,21 @@ void fa_fwd_kernel(FwdArgs a) {
   // reference). On return pp0, pp1 hold p of tile t.
   auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv) {
     if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
+    // The row max, the reference update and the exponentials form one
+    // branch-free block with the products of P(t-1), so the products run
+    // while the max is reduced. alpha = 1 exactly where the reference stays
+    // (the select also keeps -inf - -inf out).
     const float mt = tile_max(s0, s1) * c;
     const bool grow = mt > m_run + kRescaleSlack;
+    const float alpha = grow ? exp2_hw(m_run - mt) : 1.f;  // 0 where m was -inf
+    m_run = grow ? mt : m_run;
+    l_run *= alpha;
     const bool any_grow = __any(grow);
-    float alpha = 1.f;
-    if (any_grow) {
-      const float m_new = grow ? mt : m_run;
-      alpha = m_new == m_run ? 1.f : exp2_hw(m_run - m_new);  // (also for m = -inf)
-      m_run = m_new;
-      l_run *= alpha;
-    }
     exps(s0, s1);
     if (with_pv) {
       pv(vb);
-      // Each product of P(t-1) with its two V^T reads and a share of this
-      // tile's exponentials.
+      // Each product of P(t-1) with its two V^T reads and a share of the max
+      // reduction and this tile's exponentials.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < 4 * C::DT; ++i) {
