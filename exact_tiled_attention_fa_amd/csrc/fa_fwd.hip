@@ -14,8 +14,9 @@
 //     so one wave's softmax arithmetic overlaps the other's matrix products.
 //   * K/V tiles of 64 keys go HBM -> LDS with direct loads
 //     (global_load_lds_dwordx4: lane l of a wave fills bytes 16 l .. 16 l + 15
-//     of a 1 KiB block), double buffered; the loads of tile t+1 are issued
-//     before the math of tile t and waited for at the next tile's barrier.
+//     of a 1 KiB block), double buffered; the loads of K(t+1) and V(t) are
+//     placed among the matrix products of step t (each one holds up its
+//     wave's issue for a while) and waited for at the next step's barrier.
 //   * Scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16
 //     (A = K from LDS, B = Q^T held in registers for the whole sweep). In the
 //     result each lane holds 16 keys of ONE query row, so the row max and row
@@ -27,9 +28,9 @@
 //     reference max m moves (and O and l are rescaled by 2^(m_old - m_new))
 //     only when a tile's max exceeds it by more than 8, so most tiles skip the
 //     rescale; the result is the same for any reference.
-//   * Causal: K/V tiles past the block's last row are never loaded; a wave
-//     skips the math of tiles wholly above its rows; only the diagonal tiles
-//     (and a ragged tail) take the masked path.
+//   * Causal: K/V tiles past the block's last row are never loaded; every
+//     wave takes every tile of its block, and only the diagonal tiles (and a
+//     ragged tail) take the masked path.
 //   * Grid: logical id -> (batch, head, query block) with the query blocks of
 //     a head adjacent (heaviest first when causal), and logical ids laid out so
 //     that each XCD gets one contiguous range: a head's K/V is then shared in
@@ -145,6 +146,20 @@ void fa_fwd_kernel(FwdArgs a) {
     }
   };
 
+  // Steps whose K(t+1) and V(t) tiles are both full place their loads among
+  // the matrix products (block x of K before k-step kx(x) of the scores,
+  // block x of V before key group vx(x) of the PV products) instead of all at
+  // the start of the step: every direct load holds up its wave's instruction
+  // issue for a while, and spread out these stalls overlap the products.
+  auto kx = [](int x) {
+    return C::BPW == 2 ? (x == 0 ? C::KK / 4 : 5 * C::KK / 8) : (2 * x + 1) * C::KK / (2 * C::BPW);
+  };
+  auto vx = [](int x) { return C::BPW >= 4 ? x : (C::BPW == 2 ? 1 + x : 2); };
+  // Tiles from the split's first key that hold 64 keys (n_tiles or, when the
+  // last tile of the sequence is partial, n_tiles - 1). Step t spreads its
+  // loads iff t + 1 < full_tiles: K(t+1) exists and both tiles are full.
+  const int full_tiles = min(n_tiles, n_keys / kFwdKeys);
+
   issue(kg, kdo, false, 0, k_lds[0]);
 
   // ---- Q^T operand of this lane's row, kept in registers for the whole sweep.
@@ -193,11 +208,17 @@ void fa_fwd_kernel(FwdArgs a) {
   // S^T = K Q^T for two 32-key sub-tiles; the two accumulation chains
   // interleave. With valu, the products also carry the packing and summing of
   // the previous tile's p (issued in the same region).
-  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu) {
+  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu, bool dma, const uint16_t* kbase,
+                    uint32_t kl0) {
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
+      if (dma) {
+#pragma unroll
+        for (int x = 0; x < C::BPW; ++x)
+          if (kk == kx(x)) dma16(kbase, kdo[x], kl0 + 1024u * x);
+      }
       const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
       const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
       s0 = mfma32(k0, qf[kk], s0);
@@ -249,11 +270,16 @@ void fa_fwd_kernel(FwdArgs a) {
 
   // O^T += V^T P^T. The V^T operand of lane l is column d = 32 dt + l%32 at the
   // same 8 keys as its P^T registers, gathered with two transposed reads of 4 keys.
-  auto pv = [&](const char* vb) {
+  auto pv = [&](const char* vb, bool dma, const uint16_t* vbase, uint32_t vl0) {
 #pragma unroll
     for (int jt = 0; jt < 2; ++jt)
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
+        if (dma) {
+#pragma unroll
+          for (int x = 0; x < C::BPW; ++x)
+            if (2 * jt + hh == vx(x)) dma16(vbase, vdo[x], vl0 + 1024u * x);
+        }
         const int rowoff = (32 * jt + 16 * hh) * C::CPR * 16;
 #pragma unroll
         for (int dt = 0; dt < C::DT; ++dt) {
@@ -292,7 +318,8 @@ void fa_fwd_kernel(FwdArgs a) {
   // work at the same time. When a row's reference max moves, l is rescaled at
   // once and O after P(t-1) V(t-1) has joined it (both were formed at the old
   // reference). On return pp0, pp1 hold p of tile t.
-  auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv) {
+  auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv, bool dma,
+                        const uint16_t* vbase, uint32_t vl0) {
     if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
     // The row max, the reference update and the exponentials form one
     // branch-free block with the products of P(t-1), so the products run
@@ -306,7 +333,7 @@ void fa_fwd_kernel(FwdArgs a) {
     const bool any_grow = __any(grow);
     exps(s0, s1);
     if (with_pv) {
-      pv(vb);
+      pv(vb, dma, vbase, vl0);
       // Each product of P(t-1) with its two V^T reads and a share of the max
       // reduction and this tile's exponentials.
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
@@ -335,40 +362,60 @@ void fa_fwd_kernel(FwdArgs a) {
   // O += V(t-1)^T P(t-1). Step n_tiles only adds V^T P of the last tile. KB =
   // t & 1 is a compile-time constant, so every LDS address is a per-lane
   // register plus an immediate.
-  auto step = [&](auto kb_c, int t, bool with_pv) {
+  // spread: the loads go among the products (t + 1 < full_tiles); otherwise
+  // they are issued at the start.
+  auto step = [&](auto kb_c, int t, bool with_pv, bool spread) {
     constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
-    issue(vg, vdo, true, t, v_lds[KB]);
+    if (!spread) {
+      if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
+      issue(vg, vdo, true, t, v_lds[KB]);
+    }
+    const uint16_t* kbase = kg + (size_t)(t + 1) * kFwdKeys * D;
+    const uint32_t kl0 = lds_addr(k_lds[KB ^ 1]) + 1024u * (uint32_t)(wave * C::BPW);
+    const uint16_t* vbase = vg + (size_t)t * kFwdKeys * D;
+    const uint32_t vl0 = lds_addr(v_lds[KB]) + 1024u * (uint32_t)(wave * C::BPW);
     __builtin_amdgcn_sched_barrier(0);
     if (with_pv) finish_p(pp0, pp1);
     f32x16 s0, s1;
-    scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1, with_pv);
+    scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1, with_pv, spread, kbase, kl0);
     // Keep the packing and summing beside the score products: without this
     // the compiler sinks them past the mask branch, next to their first use.
     if (with_pv) asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l_run));
-    softmax_pv((t_begin + t) * kFwdKeys, s0, s1, reinterpret_cast<const char*>(v_lds[KB ^ 1]), with_pv);
+    softmax_pv((t_begin + t) * kFwdKeys, s0, s1, reinterpret_cast<const char*>(v_lds[KB ^ 1]), with_pv, spread,
+               vbase, vl0);
   };
   auto last = [&](auto kb_c) {
     constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     finish_p(pp0, pp1);
-    pv(reinterpret_cast<const char*>(v_lds[KB ^ 1]));
+    pv(reinterpret_cast<const char*>(v_lds[KB ^ 1]), false, nullptr, 0u);
   };
 
   // ---- the sweep: step 0 has no product to overlap; the steps in between go
   // two per trip; the last product follows the last step.
-  step(IC<0>{}, 0, false);
+  step(IC<0>{}, 0, false, false);
   int t = 1;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(IC<1>{}, t, true);
-    step(IC<0>{}, t + 1, true);
+  for (; t + 2 < full_tiles; t += 2) {
+    step(IC<1>{}, t, true, true);
+    step(IC<0>{}, t + 1, true, true);
   }
+  // At most three steps remain: t + 2 >= full_tiles >= n_tiles - 1.
   if (t < n_tiles) {
-    step(IC<1>{}, t, true);
-    last(IC<0>{});
+    step(IC<1>{}, t, true, false);
+    if (t + 1 < n_tiles) {
+      step(IC<0>{}, t + 1, true, false);
+      if (t + 2 < n_tiles) {
+        step(IC<1>{}, t + 2, true, false);
+        last(IC<0>{});
+      } else {
+        last(IC<1>{});
+      }
+    } else {
+      last(IC<0>{});
+    }
   } else {
     last(IC<1>{});
   }
