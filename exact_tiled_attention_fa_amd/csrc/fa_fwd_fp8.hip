@@ -183,6 +183,15 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     }
   };
 
+  // As in the BF16 pass, steps whose K(t+1) and V(t) tiles are both full
+  // place their direct loads among the matrix products (block x of K before
+  // k-step kx(x) of the scores, block x of V before d tile vx(x) of the PV
+  // products) when every wave loads a block; t + 1 < full_tiles marks them.
+  constexpr bool kSpread = C::BLOCKS >= W;
+  auto kx = [](int x) { return C::KK == 1 ? 0 : (BPW == 1 ? 1 : x); };
+  auto vx = [](int x) { return BPW == 1 ? DT / 2 : 2 * x + 1; };
+  const int full_tiles = kSpread ? min(n_tiles, n_keys / kFwdKeys) : 0;
+
   issue(kg, kdo, false, 0, k_lds(0));
 
   // ---- Q^T operand: lane (row li, half g) holds bytes 64 kk + 32 g .. + 31 of
@@ -229,11 +238,17 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   f32x16 pp0, pp1;  // p of the previous tile (FP32)
   i32x8 pf;         // its P^T operand (E4M3): dword 4 jt + q holds keys 32 jt + 8 q + 4 g + 0..3
 
-  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu) {
+  auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu, bool dma, const uint8_t* kbase,
+                    uint32_t kl0) {
     s0 = f32x16{};
     s1 = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
+      if (kSpread && dma) {
+#pragma unroll
+        for (int x = 0; x < BPW; ++x)
+          if (kk == kx(x)) dma16(kbase, kdo[x], kl0 + 1024u * x);
+      }
       const uint4 a0 = *reinterpret_cast<const uint4*>(kb + koff[kk][0]);
       const uint4 a1 = *reinterpret_cast<const uint4*>(kb + koff[kk][1]);
       const uint4 b0 = *reinterpret_cast<const uint4*>(kb + koff[kk][0] + 32 * kD8);
@@ -280,9 +295,14 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 
   // O^T += V^T P^T: the V^T operand of lane l is column 32 dt + l % 32 at the
   // 32 keys of its P^T bytes, gathered with four transposed reads of 8 keys.
-  auto pv = [&](const char* vb) {
+  auto pv = [&](const char* vb, bool dma, const uint8_t* vbase, uint32_t vl0) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
+      if (kSpread && dma) {
+#pragma unroll
+        for (int x = 0; x < BPW; ++x)
+          if (dt == vx(x)) dma16(vbase, vdo[x], vl0 + 1024u * x);
+      }
       const i32x2 r0 = lds_read_tr8(vb + voff[dt]);
       const i32x2 r1 = lds_read_tr8(vb + voff[dt] + 16 * kD8);
       const i32x2 r2 = lds_read_tr8(vb + voff[dt] + 32 * kD8);
@@ -311,21 +331,20 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     }
   };
 
-  auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv) {
+  auto softmax_pv = [&](int kv0, f32x16& s0, f32x16& s1, const char* vb, bool with_pv, bool dma,
+                        const uint8_t* vbase, uint32_t vl0) {
     if ((kv0 + kFwdKeys > N) || (CAUSAL && kv0 + kFwdKeys - 1 > wave_q0)) apply_mask(kv0, s0, s1);
+    // Branch-free reference update (alpha = 1 where it stays), so the max,
+    // the exponentials and the PV products share one scheduling region.
     const float mt = tile_max(s0, s1) * c;
     const bool grow = mt > m_run + kRescaleSlack8;
+    const float alpha = grow ? exp2_hw(m_run - mt) : 1.f;
+    m_run = grow ? mt : m_run;
+    l_run *= alpha;
     const bool any_grow = __any(grow);
-    float alpha = 1.f;
-    if (any_grow) {
-      const float m_new = grow ? mt : m_run;
-      alpha = m_new == m_run ? 1.f : exp2_hw(m_run - m_new);
-      m_run = m_new;
-      l_run *= alpha;
-    }
     exps(s0, s1);
     if (with_pv) {
-      pv(vb);
+      pv(vb, dma, vbase, vl0);
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
 #pragma unroll
       for (int i = 0; i < DT; ++i) {
@@ -345,36 +364,60 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     }
   };
 
-  auto step = [&](auto kb_c, int t, bool with_pv) {
+  auto step = [&](auto kb_c, int t, bool with_pv, bool spread) {
     constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
-    if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds(KB ^ 1));
-    issue(vg, vdo, true, t, v_lds(KB));
+    if (!spread) {
+      if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds(KB ^ 1));
+      issue(vg, vdo, true, t, v_lds(KB));
+    }
+    const uint8_t* kbase = kg + (size_t)(t + 1) * kTile8;
+    const uint32_t kl0 = lds_addr(k_lds(KB ^ 1)) + 1024u * (uint32_t)(wave * BPW);
+    const uint8_t* vbase = vg + (size_t)t * kTile8;
+    const uint32_t vl0 = lds_addr(v_lds(KB)) + 1024u * (uint32_t)(wave * BPW);
     __builtin_amdgcn_sched_barrier(0);
     if (with_pv) finish_p(pp0, pp1);
     f32x16 s0, s1;
-    scores(k_lds(KB), s0, s1, with_pv);
+    scores(k_lds(KB), s0, s1, with_pv, spread, kbase, kl0);
     if (with_pv) asm volatile("" : "+v"(pf), "+v"(l_run));
-    softmax_pv((t_begin + t) * kFwdKeys, s0, s1, v_lds(KB ^ 1), with_pv);
+    softmax_pv((t_begin + t) * kFwdKeys, s0, s1, v_lds(KB ^ 1), with_pv, spread, vbase, vl0);
   };
   auto last = [&](auto kb_c) {
     constexpr int KB = decltype(kb_c)::value;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     finish_p(pp0, pp1);
-    pv(v_lds(KB ^ 1));
+    pv(v_lds(KB ^ 1), false, nullptr, 0u);
   };
 
-  step(IC<0>{}, 0, false);
+  step(IC<0>{}, 0, false, false);
   int t = 1;
-  for (; t + 1 < n_tiles; t += 2) {
-    step(IC<1>{}, t, true);
-    step(IC<0>{}, t + 1, true);
+  for (; t + 2 < full_tiles; t += 2) {
+    step(IC<1>{}, t, true, true);
+    step(IC<0>{}, t + 1, true, true);
   }
+  if (!kSpread) {
+    for (; t + 1 < n_tiles; t += 2) {
+      step(IC<1>{}, t, true, false);
+      step(IC<0>{}, t + 1, true, false);
+    }
+  }
+  // At most three steps remain (t + 2 >= full_tiles >= n_tiles - 1 when the
+  // loads spread; at most one otherwise).
   if (t < n_tiles) {
-    step(IC<1>{}, t, true);
-    last(IC<0>{});
+    step(IC<1>{}, t, true, false);
+    if (t + 1 < n_tiles) {
+      step(IC<0>{}, t + 1, true, false);
+      if (t + 2 < n_tiles) {
+        step(IC<1>{}, t + 2, true, false);
+        last(IC<0>{});
+      } else {
+        last(IC<1>{});
+      }
+    } else {
+      last(IC<0>{});
+    }
   } else {
     last(IC<1>{});
   }
