@@ -31,10 +31,10 @@
 //   * Causal: K/V tiles past the block's last row are never loaded; every
 //     wave takes every tile of its block, and only the diagonal tiles (and a
 //     ragged tail) take the masked path.
-//   * Grid: logical id -> (batch, head, query block) with the query blocks of
-//     a head adjacent (heaviest first when causal), and logical ids laid out so
-//     that each XCD gets one contiguous range: a head's K/V is then shared in
-//     one XCD's L2.
+//   * Grid: logical id -> (batch, head, query block, key split) with the
+//     query blocks of a head adjacent (heaviest first when causal), and
+//     logical ids laid out so that each XCD gets one contiguous range: a
+//     head's K/V is then shared in one XCD's L2.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -85,15 +85,18 @@ void fa_fwd_kernel(FwdArgs a) {
   const int g = lane >> 5;    // half of the wave (k-slot group)
   const int li = lane & 31;   // query row within the wave / column of S^T
 
-  // ---- grid order: XCD-contiguous; head-major, then key split, then query
-  // block (heaviest first when causal), so the blocks sharing one K/V chunk sit
-  // together on one XCD.
+  // ---- grid order: XCD-contiguous; head-major, then query block (heaviest
+  // first when causal), then key split. Without splits a head's blocks sit
+  // together on one XCD and share its K/V in that L2; with splits each XCD
+  // takes all splits of a few blocks, so it reads only those blocks' Q when
+  // every work-group starts at once (8 XCDs reading all of Q cost the 1-head
+  // 8K call 4%), while K/V chunks are streamed once per XCD.
   const int lid = xcd_contiguous(blockIdx.x, a.nwg);
   const int per_head = a.nqb * a.n_splits;
   const int bh = lid / per_head;
   const int rem = lid - bh * per_head;
-  const int split = rem / a.nqb;
-  int qb = rem - split * a.nqb;
+  int qb = rem / a.n_splits;
+  const int split = rem - qb * a.n_splits;
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;

@@ -127,14 +127,14 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   const int g = lane >> 5;
   const int li = lane & 31;
 
-  // ---- grid order (as the BF16 pass): XCD-contiguous, head-major, then key
-  // split, then query block (heaviest first when causal).
+  // ---- grid order (as the BF16 pass): XCD-contiguous, head-major, then query
+  // block (heaviest first when causal), then key split.
   const int lid = xcd_contiguous(blockIdx.x, a.nwg);
   const int per_head = a.nqb * a.n_splits;
   const int bh = lid / per_head;
   const int rem = lid - bh * per_head;
-  const int split = rem / a.nqb;
-  int qb = rem - split * a.nqb;
+  int qb = rem / a.n_splits;
+  const int split = rem - qb * a.n_splits;
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
