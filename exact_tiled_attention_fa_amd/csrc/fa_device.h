@@ -118,85 +118,86 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
 }
 
 // Log-sum-exp merge of one row's S key-split partials (BF16 normalised
-// outputs O_s and FP32 lse_s, natural log) for four columns: M = max_s lse_s,
+// outputs O_s and FP32 lse_s, natural log) for eight columns: M = max_s lse_s,
 // w_s = e^(lse_s - M), O = sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s.
-// op points at column col of partial 0 (partials D values apart), lp at the
-// row's S lse values. With S <= 8 all loads go out together (the partials do
-// not depend on the lse values); otherwise eight partials at a time after a
-// first pass for M. O goes to o4 (four BF16, nearest even); lse is written
-// when write_lse.
+// op points at column col of partial 0 (partials D values apart, col a
+// multiple of 8, so each partial is one 16-byte load), lp at the row's S lse
+// values. With S <= 8 all loads go out together (the partials do not depend
+// on the lse values); otherwise eight partials at a time after a first pass
+// for M. O goes to o8 (eight BF16, nearest even); lse is written when
+// write_lse.
 template <int D>
-__device__ __forceinline__ void merge_splits4(const uint16_t* __restrict__ op, const float* __restrict__ lp, int S,
-                                              uint16_t* __restrict__ o4, float* __restrict__ lse_out,
+__device__ __forceinline__ void merge_splits8(const uint16_t* __restrict__ op, const float* __restrict__ lp, int S,
+                                              uint16_t* __restrict__ o8, float* __restrict__ lse_out,
                                               bool write_lse) {
-  auto part = [&](int s) {
-    const uint2 w = *reinterpret_cast<const uint2*>(op + (size_t)s * D);
-    return make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+  auto part = [&](int s, float* v) {
+    const uint4 w = *reinterpret_cast<const uint4*>(op + (size_t)s * D);
+    v[0] = bf16_lo(w.x); v[1] = bf16_hi(w.x); v[2] = bf16_lo(w.y); v[3] = bf16_hi(w.y);
+    v[4] = bf16_lo(w.z); v[5] = bf16_hi(w.z); v[6] = bf16_lo(w.w); v[7] = bf16_hi(w.w);
   };
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  float M = -INFINITY;
   if (S <= 8) {
     float l[8];
-    float4 v[8];
+    float v[8][8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const bool in = u < S;
       l[u] = in ? lp[u] : -INFINITY;
-      v[u] = in ? part(u) : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-    float M = l[0];
+      if (in) {
+        part(u, v[u]);
+      } else {
 #pragma unroll
-    for (int u = 1; u < 8; ++u) M = fmaxf(M, l[u]);
+        for (int c = 0; c < 8; ++c) v[u][c] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) M = fmaxf(M, l[u]);
     const float Ms = M == -INFINITY ? 0.f : M;
-    float wsum = 0.f;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const float w = u < S ? exp2_hw((l[u] - Ms) * kLog2e) : 0.f;
       wsum += w;
-      acc.x = fmaf(w, v[u].x, acc.x);
-      acc.y = fmaf(w, v[u].y, acc.y);
-      acc.z = fmaf(w, v[u].z, acc.z);
-      acc.w = fmaf(w, v[u].w, acc.w);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, v[u][c], acc[c]);
     }
-    const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-    *reinterpret_cast<uint2*>(o4) = pack_bf16x4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
-    if (write_lse) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
-    return;
-  }
-  float M = -INFINITY;
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float l[8];
+  } else {
+    for (int s0 = 0; s0 < S; s0 += 8) {
 #pragma unroll
-    for (int u = 0; u < 8; ++u) l[u] = s0 + u < S ? lp[s0 + u] : -INFINITY;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) M = fmaxf(M, l[u]);
-  }
-  const float Ms = M == -INFINITY ? 0.f : M;
-  float wsum = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s0 = 0; s0 < S; s0 += 8) {
-    float4 v[8];
-    float w[8];
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const bool in = s0 + u < S;
-      v[u] = in ? part(s0 + u) : make_float4(0.f, 0.f, 0.f, 0.f);
-      w[u] = in ? exp2_hw((lp[s0 + u] - Ms) * kLog2e) : 0.f;
+      for (int u = 0; u < 8; ++u) M = fmaxf(M, s0 + u < S ? lp[s0 + u] : -INFINITY);
     }
+    const float Ms = M == -INFINITY ? 0.f : M;
+    for (int s0 = 0; s0 < S; s0 += 8) {
+      float v[8][8];
+      float w[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      wsum += w[u];
-      acc.x = fmaf(w[u], v[u].x, acc.x);
-      acc.y = fmaf(w[u], v[u].y, acc.y);
-      acc.z = fmaf(w[u], v[u].z, acc.z);
-      acc.w = fmaf(w[u], v[u].w, acc.w);
+      for (int u = 0; u < 8; ++u) {
+        const bool in = s0 + u < S;
+        if (in) {
+          part(s0 + u, v[u]);
+        } else {
+#pragma unroll
+          for (int c = 0; c < 8; ++c) v[u][c] = 0.f;
+        }
+        w[u] = in ? exp2_hw((lp[s0 + u] - Ms) * kLog2e) : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        wsum += w[u];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) acc[c] = fmaf(w[u], v[u][c], acc[c]);
+      }
     }
   }
   const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
-  *reinterpret_cast<uint2*>(o4) = pack_bf16x4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  const uint2 lo = pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  const uint2 hi = pack_bf16x4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+  *reinterpret_cast<uint4*>(o8) = make_uint4(lo.x, lo.y, hi.x, hi.y);
   if (write_lse) *lse_out = wsum > 0.f ? M + log2_hw(wsum) * kLn2 : -INFINITY;
 }
 
-// Threads per work-group of the merge kernels (D / 4 lanes per row).
+// Threads per work-group of the forward merge kernel (D / 8 lanes per row).
 constexpr int kMergeThreads = 256;
 
 // 16 bytes per lane from global memory straight into LDS: lane l of the wave

@@ -469,23 +469,23 @@ void fa_fwd_kernel(FwdArgs a) {
   }
 }
 
-// Merge each row's non-empty key splits with the log-sum-exp combine; D / 4
-// lanes take one row, four columns each, so every partial row is one
-// coalesced 16-byte-per-lane load.
+// Merge each row's non-empty key splits with the log-sum-exp combine; D / 8
+// lanes take one row, eight columns each, so every partial of a row is one
+// 16-byte load per lane.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kMergeThreads) void fa_fwd_combine_kernel(FwdArgs a) {
-  constexpr int LPR = D / 4;                 // lanes per row
+  constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPG = kMergeThreads / LPR;   // rows per work-group
   const size_t rows = (size_t)a.B * a.Hq * a.N;
   const size_t row = (size_t)blockIdx.x * RPG + threadIdx.x / LPR;
   if (row >= rows) return;
-  const int col = 4 * (threadIdx.x % LPR);
+  const int col = 8 * (threadIdx.x % LPR);
   const int n = (int)(row % (size_t)a.N);
   const int qb = n / a.rows;
   const int kv_end = CAUSAL ? min(a.N, qb * a.rows + a.rows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
   const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
-  merge_splits4<D>(a.o_part + row * a.n_splits * D + col, a.lse_part + row * a.n_splits, S, a.o + row * D + col,
+  merge_splits8<D>(a.o_part + row * a.n_splits * D + col, a.lse_part + row * a.n_splits, S, a.o + row * D + col,
                    a.lse + row, col == 0);
 }
 
@@ -509,7 +509,7 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) 
 template <int D, bool CAUSAL>
 static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t stream) {
   const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t per_wg = kMergeThreads / (D / 4);
+  const size_t per_wg = kMergeThreads / (D / 8);
   hipLaunchKernelGGL((fa_fwd_combine_kernel<D, CAUSAL>), dim3((unsigned)((rows + per_wg - 1) / per_wg)),
                      dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
