@@ -100,6 +100,7 @@ int check_fwd_sizes(int B, int Hq, int N, int d) {
 
 struct FwdPlan {
   int rows, nqb, n_splits, split_tiles;
+  int head_group;    // see FwdArgs::head_group
   int64_t nwg;       // work-groups of the forward launch
   size_t ws_bytes;   // partial-result buffer for a split, 0 otherwise
 };
@@ -111,6 +112,12 @@ FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal) {
   FwdPlan p;
   const int waves = fa::fwd_waves(causal, N, (int64_t)B * Hq * ((N + 255) / 256), device_cu_count());
   p.rows = fa::kFwdWaveRows * waves;
+  // Causal blocks differ in work (heaviest first). Each of the 8 XCDs takes a
+  // contiguous range of the grid; when that range is a whole number (>= 2) of
+  // heads, their blocks interleave so the XCD starts all its heaviest blocks
+  // first instead of one head's after another's lightest.
+  const int64_t nbh = (int64_t)B * Hq;
+  p.head_group = causal && nbh % 8 == 0 && nbh >= 16 ? (int)(nbh / 8) : 1;
   p.nqb = (N + p.rows - 1) / p.rows;
   const int64_t base = (int64_t)B * Hq * p.nqb;
   const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
@@ -147,6 +154,7 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.nwg = (int)p.nwg;
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
+  a.head_group = p.head_group;
   a.o_part = static_cast<uint16_t*>(ws);
   a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = 1.f;
@@ -224,6 +232,7 @@ int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const
   a.nwg = (int)p.nwg;
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
+  a.head_group = p.head_group;
   a.o_part = static_cast<uint16_t*>(ws);
   a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = v_scale;

@@ -127,14 +127,18 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   const int g = lane >> 5;
   const int li = lane & 31;
 
-  // ---- grid order (as the BF16 pass): XCD-contiguous, head-major, then query
-  // block (heaviest first when causal), then key split.
+  // ---- grid order (as the BF16 pass): XCD-contiguous, groups of head_group
+  // heads, then query block (heaviest first when causal), then head within
+  // the group, then key split.
   const int lid = xcd_contiguous(blockIdx.x, a.nwg);
   const int per_head = a.nqb * a.n_splits;
-  const int bh = lid / per_head;
-  const int rem = lid - bh * per_head;
-  int qb = rem / a.n_splits;
-  const int split = rem - qb * a.n_splits;
+  const int grp = lid / (a.head_group * per_head);
+  const int rem_g = lid - grp * a.head_group * per_head;
+  const int gh = min(a.head_group, a.B * a.Hq - grp * a.head_group);  // heads in this group
+  const int qs = rem_g / gh;
+  const int bh = grp * a.head_group + (rem_g - qs * gh);
+  int qb = qs / a.n_splits;
+  const int split = qs - qb * a.n_splits;
   if (CAUSAL) qb = a.nqb - 1 - qb;
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;

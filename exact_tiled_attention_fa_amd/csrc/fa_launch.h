@@ -31,6 +31,7 @@ struct FwdArgs {
   uint16_t* o_part;  // [B*Hq*N, n_splits, d] BF16 normalised partial outputs
   float* lse_part;   // [B*Hq*N, n_splits] FP32
   float v_scale;  // FP8 pass: the factor of V's codes (O = v_scale P V / l)
+  int head_group;  // heads whose blocks interleave in the grid order (one XCD's share; 1 = head by head)
 };
 constexpr int kFwdKeys = 64;      // keys per K/V tile
 constexpr int kFwdWaveRows = 32;  // query rows per wave
