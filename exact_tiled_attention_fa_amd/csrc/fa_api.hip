@@ -322,6 +322,14 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.scale = scale;
   a.nkb = (int)nkb;
   a.nqb = (int)nqb;
+  // Causal blocks differ in work; when one XCD's range of the grid is a whole
+  // number (>= 2) of heads, their blocks interleave (heaviest of all first),
+  // as in the forward.
+  const auto head_group = [&](int64_t heads) {
+    return causal && heads % 8 == 0 && heads >= 16 ? (int)(heads / 8) : 1;
+  };
+  a.hg_kv = head_group((int64_t)B * Hkv);
+  a.hg_q = head_group((int64_t)B * Hq);
   const hipError_t e = fa::launch_bwd(a, d, causal != 0, reinterpret_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
 }

@@ -130,11 +130,16 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   const int b16 = lane >> 4;  // 16-lane block
   const int j16 = lane & 15;
 
-  // Grid: XCD-contiguous; KV heads outermost, then key blocks (the first key
-  // blocks have the most query tiles when causal, so they start first).
+  // Grid: XCD-contiguous; groups of hg_kv KV heads, then key blocks (the
+  // first key blocks have the most query tiles when causal, so they start
+  // first), then head within the group: a causal XCD range of several heads
+  // starts all their heaviest blocks first.
   const int lid = xcd_contiguous(blockIdx.x, nwg);
-  const int bhk = lid / a.nkb;
-  const int kb = lid - bhk * a.nkb;
+  const int grp = lid / (a.hg_kv * a.nkb);
+  const int rem_g = lid - grp * a.hg_kv * a.nkb;
+  const int gh = min(a.hg_kv, a.B * a.Hkv - grp * a.hg_kv);  // KV heads in this group
+  const int kb = rem_g / gh;
+  const int bhk = grp * a.hg_kv + (rem_g - kb * gh);
   const int b = bhk / a.Hkv;
   const int hk = bhk - b * a.Hkv;
   const int G = a.Hq / a.Hkv;
@@ -290,8 +295,11 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const int li = lane & 31;
 
   const int lid = xcd_contiguous(blockIdx.x, nwg);
-  const int bh = lid / a.nqb;
-  int qb = lid - bh * a.nqb;
+  const int grp = lid / (a.hg_q * a.nqb);
+  const int rem_g = lid - grp * a.hg_q * a.nqb;
+  const int gh = min(a.hg_q, a.B * a.Hq - grp * a.hg_q);  // query heads in this group
+  int qb = rem_g / gh;
+  const int bh = grp * a.hg_q + (rem_g - qb * gh);
   if (CAUSAL) qb = a.nqb - 1 - qb;  // heaviest first
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;

@@ -79,6 +79,8 @@ struct BwdArgs {
   float scale;
   int nkb;       // 64-key blocks per KV head
   int nqb;       // 128-row query blocks per head
+  int hg_kv;     // KV heads whose key blocks interleave in the dK/dV grid order (1 = head by head)
+  int hg_q;      // query heads whose row blocks interleave in the dQ grid order
 };
 constexpr int kBwdKeyBlock = 64;
 constexpr int kBwdRowBlock = 128;
