@@ -56,6 +56,13 @@ def test_bwd_small(B, Hq, Hkv, N, causal):
     _run_small(B, Hq, Hkv, N, causal, seed=700 + N + Hq)
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(2, 16, 8, 300), (1, 24, 24, 130)])
+def test_bwd_causal_head_groups(B, Hq, Hkv, N):
+    """Causal grids interleave the blocks of one XCD's share of heads: here
+    2 KV heads and 4 query heads per group, then 3 and 3."""
+    _run_small(B, Hq, Hkv, N, True, seed=1400 + N + Hq)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.3])
 def test_bwd_scale_edge_cases(scale):
     _run_small(1, 2, 1, 300, True, seed=800, scale=scale)

@@ -74,6 +74,14 @@ def test_causal_8k_many_heads():
     _run_case(si.FwdCase("1x8x8192 d128 causal", 1, 8, 8, 8192, 128, True, seed=41, sampled_rows=256))
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 24, 24, 300, 64), (2, 8, 4, 500, 128), (1, 16, 2, 190, 128)])
+def test_causal_head_groups(B, Hq, Hkv, N, d):
+    """Causal grids whose B*Hq is a multiple of 8 (>= 16) interleave the blocks
+    of B*Hq/8 heads in the grid order (groups of 3, 2 and 2 heads here)."""
+    _run_case(si.FwdCase(f"head groups B{B} Hq{Hq} Hkv{Hkv} N{N} d{d}", B, Hq, Hkv, N, d, True,
+                         seed=1300 + Hq + N))
+
+
 @pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
