@@ -12,7 +12,9 @@ the clock and address translation reach steady state. `value` is the non-causal 
 per call over the call's average duration, measured with HIP events on the
 stream the kernels run on around K back-to-back calls (a call is the forward
 kernel, plus the combine kernel when the keys are split). The decode rate is
-reported as algorithmic HBM GB/s (K and V read once per KV head).
+reported as algorithmic HBM GB/s (K and V read once per KV head). The "also"
+section adds other workloads and, for the step's three calls, cold-cache
+timings (median and minimum of 50 single calls, each after writing 1 GiB).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy kernel of known size, for
@@ -297,6 +299,31 @@ def main() -> int:
 
     extra = {}
     if not args.no_extra:
+        # Cold caches: before each of 50 single calls a 1 GiB buffer is written
+        # (more than the 256 MiB last-level cache), then the call is timed
+        # alone with events on the kernels' stream; median and minimum.
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        for key, fn, fl in (("fwd_1x1x8192_d128_cold", run_fwd, flops),
+                            ("fwd_1x1x8192_d128_causal_cold", run_fwd_c, flops / 2),
+                            ("decode_B16_Hq32_Hkv8_L8192_cold", run_dec, None)):
+            times = []
+            for i in range(50):
+                flush.fill_(i & 0xFF)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b) * 1e-3)
+            times.sort()
+            med, best = times[len(times) // 2], times[0]
+            if fl is None:
+                extra[key] = {"us_median": round(med * 1e6, 2), "us_min": round(best * 1e6, 2),
+                              "hbm_gbs_median": round(kv_bytes / med / 1e9, 1)}
+            else:
+                extra[key] = {"us_median": round(med * 1e6, 2), "us_min": round(best * 1e6, 2),
+                              "tflops_median": round(fl / med / 1e12, 2)}
+        del flush
         for case in (si.HEADS32_4K, si.HEADS32_4K_CAUSAL):
             q3, k3, v3 = (up(x) for x in si.fwd_inputs(case))
             o3 = torch.empty_like(q3)
