@@ -18,7 +18,8 @@
 //     instruction); Q^T of up to 16 grouped heads is the B operand, kept in
 //     registers. Lane l then holds head l%16 at 4 keys per 16-key tile.
 //   * Online softmax per head in base 2, reduced over the 4 lanes of a head.
-//   * K and V are read once, with non-temporal loads.
+//   * K and V are read once; V (whole 128-byte lines per load) with the
+//     non-temporal hint, K (half lines per load) without it.
 //   * P V on the vector ALUs: V is loaded with fully coalesced 16-byte reads
 //     (one row per 16 lanes at d = 128), each lane keeps FP32 partial outputs
 //     for its 8 columns and every head of the group; the weights p[key][head]
@@ -219,13 +220,18 @@ void fa_decode_split_kernel(DecArgs a) {
     const int kw = kb + wave * kDecWaveKeys;
     // ---- loads: K in MFMA A layout, V coalesced. Rows past the chunk read the
     // chunk's last key instead (finite data): their scores become -inf, p = 0.
+    // K takes plain loads: a K load fetches 64 bytes of each of 16 rows, the
+    // other half of each 128-byte line comes with the next k-step's load, and
+    // with the non-temporal hint that second half missed again (streaming the
+    // decode's loads alone: 6.3 TB/s with the hint on K, 7.4 without). V loads
+    // take whole lines and keep the hint.
     bf16x8 kf[2][C::KK];
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
       const int key = min(kw + tt * 16 + n, key_end - 1);
       const uint4* krow = reinterpret_cast<const uint4*>(a.k + kv_base + (size_t)key * D);
 #pragma unroll
-      for (int kk = 0; kk < C::KK; ++kk) kf[tt][kk] = __builtin_bit_cast(bf16x8, load_nt(krow + 4 * kk + quad));
+      for (int kk = 0; kk < C::KK; ++kk) kf[tt][kk] = __builtin_bit_cast(bf16x8, krow[4 * kk + quad]);
     }
     uint4 vr[C::NV];
 #pragma unroll
