@@ -76,6 +76,13 @@ void fa_fwd_kernel(FwdArgs a) {
   // output rows here for coalesced stores (one wave's 32 BF16 rows take half
   // a tile, so eight waves fit).
   __shared__ uint4 smem[4][C::TILE_CHUNKS];
+  // With 8 waves (one work-group per CU, so LDS is to spare) each wave stages
+  // its 32 Q rows here by direct loads (rows XOR-swizzled as K) and reads its
+  // operand from them: loading the operand layout straight from HBM takes 32
+  // bytes of 32 rows per load, and at the start of every work-group those
+  // requests held up step 0 by about a microsecond (3% of the 1-head 8K call).
+  constexpr bool kStageQ = W == 8;
+  __shared__ uint4 q_lds[kStageQ ? W * 32 * C::CPR : 1];
   uint4 (*k_lds)[C::TILE_CHUNKS] = smem;
   uint4 (*v_lds)[C::TILE_CHUNKS] = smem + 2;
 
@@ -181,7 +188,18 @@ void fa_fwd_kernel(FwdArgs a) {
   const uint32_t sign = a.c < 0.f ? 0x80008000u : 0u;
   const float c = fmaxf(fabsf(a.c), 1.17549435e-38f);
   bf16x8 qf[C::KK];
-  {
+  if constexpr (kStageQ) {
+    // Rows past N repeat row N - 1 (finite; their results are never stored).
+    const int wrow0 = min(q0 + wave * 32, N - 1);
+    const uint16_t* qsrc = a.q + qo_base + (size_t)wrow0 * D;
+    const uint32_t ql0 = lds_addr(q_lds) + (uint32_t)(wave * 32 * D * 2);
+#pragma unroll
+    for (int x = 0; x < 32 / C::RPB; ++x) {
+      const int r = x * C::RPB + dma_row;
+      const int rel = min(q0 + wave * 32 + r, N - 1) - wrow0;
+      dma16(qsrc, 2u * (uint32_t)(rel * D + 8 * (dma_p ^ kswz<D>(r))), ql0 + 1024u * x);
+    }
+  } else {
     const uint4* qrow = reinterpret_cast<const uint4*>(a.q + qo_base + (size_t)(qi < N ? qi : 0) * D);
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
@@ -190,6 +208,17 @@ void fa_fwd_kernel(FwdArgs a) {
       qf[kk] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // Staged Q: this lane's operand (row li, chunks 2 kk + g) once step 0's
+  // wait and barrier have passed.
+  auto read_q = [&]() {
+    const char* qb = reinterpret_cast<const char*>(q_lds) + wave * 32 * D * 2 + li * D * 2;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      uint4 w = *reinterpret_cast<const uint4*>(qb + 16 * ((2 * kk + g) ^ kswz<D>(li)));
+      w.x ^= sign; w.y ^= sign; w.z ^= sign; w.w ^= sign;
+      qf[kk] = __builtin_bit_cast(bf16x8, w);
+    }
+  };
 
   // ---- per-lane LDS byte offsets (tile-relative). K: row li, chunk 2 kk + g.
   // V^T: lane t16 of each 16-lane block names row t16 / 4 of a 4-key group and
@@ -382,6 +411,7 @@ void fa_fwd_kernel(FwdArgs a) {
       if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
       issue(vg, vdo, true, t, v_lds[KB]);
     }
+    if (kStageQ && !with_pv) read_q();
     const uint16_t* kbase = kg + (size_t)(t + 1) * kFwdKeys * D;
     const uint32_t kl0 = lds_addr(k_lds[KB ^ 1]) + 1024u * (uint32_t)(wave * C::BPW);
     const uint16_t* vbase = vg + (size_t)t * kFwdKeys * D;
