@@ -117,6 +117,13 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   // each wave's 32 BF16 rows over the whole array.
   constexpr int STAGE_BYTES = W * 32 * kD8 * 2 > 4 * kTile8 ? W * 32 * kD8 * 2 : 4 * kTile8;
   __shared__ uint4 smem[STAGE_BYTES / 16];
+  // Q rows staged in LDS by direct loads (as the BF16 pass) at d = 128 where
+  // LDS allows: one work-group per CU (8 waves), or two with room for both.
+  // (At d = 64 the direct operand loads are only two per lane and staging
+  // measured 1.5% slower.)
+  constexpr int Q_BYTES = W * 32 * kD8;
+  constexpr bool kStageQ = D == 128 && (W == 8 || 2 * (STAGE_BYTES + Q_BYTES) <= 160 * 1024);
+  __shared__ uint4 q_lds[kStageQ ? Q_BYTES / 16 : 1];
   char* const lds = reinterpret_cast<char*>(smem);
   auto k_lds = [&](int i) { return lds + i * kTile8; };
   auto v_lds = [&](int i) { return lds + (2 + i) * kTile8; };
@@ -206,7 +213,18 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   const int sign = a.c < 0.f ? (int)0x80808080u : 0;
   const float c = fmaxf(fabsf(a.c), 1.17549435e-38f);
   i32x8 qf[C::KK];
-  {
+  if constexpr (kStageQ) {
+    // Rows past N repeat row N - 1 (finite; their results are never stored).
+    const int wrow0 = min(q0 + wave * 32, N - 1);
+    const uint8_t* qsrc = q8 + ((size_t)(b * a.Hq + h) * N + wrow0) * kD8;
+    const uint32_t ql0 = lds_addr(q_lds) + (uint32_t)(wave * 32 * kD8);
+#pragma unroll
+    for (int x = 0; x < 32 / RPB; ++x) {
+      const int r = x * RPB + dma_row;
+      const int rel = min(q0 + wave * 32 + r, N - 1) - wrow0;
+      dma16(qsrc, (uint32_t)(rel * kD8 + 16 * (dma_p ^ kswz8<D>(r))), ql0 + 1024u * x);
+    }
+  } else {
     const uint4* qrow = reinterpret_cast<const uint4*>(q8 + ((size_t)(b * a.Hq + h) * N + (qi < N ? qi : 0)) * kD8);
 #pragma unroll
     for (int kk = 0; kk < C::KK; ++kk) {
@@ -216,6 +234,18 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
                      (int)w1.x ^ sign, (int)w1.y ^ sign, (int)w1.z ^ sign, (int)w1.w ^ sign};
     }
   }
+  // Staged Q: this lane's operand (row li, chunks 4 kk + 2 g + {0, 1}) once
+  // step 0's wait and barrier have passed.
+  auto read_q = [&]() {
+    const char* qb = reinterpret_cast<const char*>(q_lds) + wave * 32 * kD8 + li * kD8;
+#pragma unroll
+    for (int kk = 0; kk < C::KK; ++kk) {
+      const uint4 w0 = *reinterpret_cast<const uint4*>(qb + 16 * ((4 * kk + 2 * g) ^ kswz8<D>(li)));
+      const uint4 w1 = *reinterpret_cast<const uint4*>(qb + 16 * ((4 * kk + 2 * g + 1) ^ kswz8<D>(li)));
+      qf[kk] = i32x8{(int)w0.x ^ sign, (int)w0.y ^ sign, (int)w0.z ^ sign, (int)w0.w ^ sign,
+                     (int)w1.x ^ sign, (int)w1.y ^ sign, (int)w1.z ^ sign, (int)w1.w ^ sign};
+    }
+  };
 
   // ---- per-lane LDS byte offsets. K: row li, logical chunks 4 kk + 2 g + {0, 1}
   // (rows 32 + li add 4 KiB). V^T: as a source lane, lane i of 16-lane block
@@ -376,6 +406,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
       if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds(KB ^ 1));
       issue(vg, vdo, true, t, v_lds(KB));
     }
+    if (kStageQ && !with_pv) read_q();
     const uint8_t* kbase = kg + (size_t)(t + 1) * kTile8;
     const uint32_t kl0 = lds_addr(k_lds(KB ^ 1)) + 1024u * (uint32_t)(wave * BPW);
     const uint8_t* vbase = vg + (size_t)t * kTile8;
