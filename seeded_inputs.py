@@ -182,3 +182,17 @@ def sample_rows(seed: int, head: int, N: int, count: int, boundary: int = 64) ->
     pool = np.setdiff1d(np.arange(N, dtype=np.int64), np.array(forced, dtype=np.int64))
     extra = rng.choice(pool, size=count - len(forced), replace=False)
     return np.sort(np.concatenate([np.array(forced, dtype=np.int64), extra]))
+
+
+def growing_score_inputs(N: int, d: int, H: int = 2, seed: int = 1500):
+    """Q with first component 4 and K with first component 0.4 j sqrt(d/128)
+    (N(0,1) elsewhere), float32: at scale 1/sqrt(d) the scores of a row grow
+    by about 10 in base 2 per 64 keys, so a running maximum taken 64 keys at
+    a time rises on every step."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((1, H, N, d), dtype=np.float32)
+    k = rng.standard_normal((1, H, N, d), dtype=np.float32)
+    v = rng.standard_normal((1, H, N, d), dtype=np.float32)
+    q[..., 0] = 4.0
+    k[..., 0] = 0.4 * np.arange(N, dtype=np.float32)[None, None, :] * math.sqrt(d / 128.0)
+    return q, k, v

@@ -82,6 +82,31 @@ def test_causal_head_groups(B, Hq, Hkv, N, d):
                          seed=1300 + Hq + N))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_growing_scores_rescale_every_tile(d, causal):
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    N = 640
+    q, k, v = si.growing_score_inputs(N, d, seed=1500 + d)
+    qb, kb, vb = si.bf16_round_bits(q), si.bf16_round_bits(k), si.bf16_round_bits(v)
+    scale = 1.0 / math.sqrt(d)
+    _say(f"[fwd] growing scores N{N} d{d} causal={causal}")
+    o, lse = fa.fwd(to_dev(qb), to_dev(kb), to_dev(vb), causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    o_np, lse_np = to_f64(o), to_f64(lse)
+    qf, kf, vf = si.bf16_bits_to_f32(qb), si.bf16_bits_to_f32(kb), si.bf16_bits_to_f32(vb)
+    vx = np.concatenate([vf, np.abs(vf)], axis=-1)
+    ox_ref, lse_ref = fa_oracle.attention_ref(qf, kf, vx, causal, scale)
+    o_ref, pabs_ref = ox_ref[..., :d], ox_ref[..., d:]
+    # The last key of each row dominates; still, every tile raised the max.
+    s_last = qf[0, 0, :, 0].astype(np.float64) * kf[0, 0, -1, 0] * scale * math.log2(math.e)
+    assert s_last.min() > 8 * (N // 64)
+    split = fa.fwd_workspace_bytes(1, 2, N, d) > 0
+    check_o(o_np, o_ref, pabs_ref, f"growing N{N} d{d}", flat_gate=False, split=split)
+    check_lse(lse_np, lse_ref, f"growing N{N} d{d}")
+
+
 @pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 1000])
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])

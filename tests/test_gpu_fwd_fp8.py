@@ -81,13 +81,13 @@ def _bounds(q8, k8, v8, qs, ks, vs, causal, scale, rows, o_ref, p, split):
     return out
 
 
-def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0, d=128):
+def _run(name, B, Hq, Hkv, N, causal, seed, scale=None, sampled=None, q_sign=1.0, d=128, codes=None):
     import torch
     import exact_tiled_attention_fa_amd as fa
     case = si.FwdCase(name, B, Hq, Hkv, N, d, causal, seed)
     scale = case.scale if scale is None else scale
     _say(f"[fp8] {name} B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal} seed={seed} scale={scale}")
-    q8, k8, v8, qs, ks, vs = si.fwd_fp8_inputs(case)
+    q8, k8, v8, qs, ks, vs = si.fwd_fp8_inputs(case) if codes is None else codes
     qs *= q_sign
     q, k, v = _upload(q8), _upload(k8), _upload(v8)
     o, lse = fa.fwd_fp8(q, k, v, qs, ks, vs, causal=causal, scale=scale)
@@ -166,3 +166,19 @@ def test_fp8_d64_key_split_gqa(causal):
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_d64_32_heads_4k(causal):
     _run("1x32x4096 d64", 1, 32, 32, 4096, causal, seed=4, sampled=96, d=64)
+
+
+def _quantize(x):
+    """Per-tensor E4M3 codes of x (amax maps to 448) and the dequantisation factor."""
+    descale = float(np.abs(x).max()) / si.FP8_E4M3_MAX
+    return si.fp8_e4m3_round_bits(x / descale), descale
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_growing_scores_rescale(causal):
+    """Scores that grow by about 10 (base 2) per 64-key tile: the FP8 pass's
+    row max (slack 2) moves on every tile, so O and l are rescaled each step."""
+    N, d = 640, 128
+    q, k, v = si.growing_score_inputs(N, d, seed=1600)
+    (q8, qs), (k8, ks), (v8, vs) = _quantize(q), _quantize(k), _quantize(v)
+    _run(f"growing N{N}", 1, 2, 2, N, causal, seed=1600, d=d, codes=(q8, k8, v8, qs, ks, vs))
