@@ -6,6 +6,7 @@ silently runs anywhere but the HIP kernels.
 from __future__ import annotations
 
 import ctypes
+import operator
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -29,28 +30,50 @@ class FaError(RuntimeError):
         super().__init__(f"{where}: {msg} (status {status})")
 
 
+class _Int32(ctypes.c_int):
+    """int argument that raises instead of wrapping (plain c_int keeps the low 32 bits)."""
+
+    @classmethod
+    def from_param(cls, value):
+        value = operator.index(value)
+        if not -(1 << 31) <= value < (1 << 31):
+            raise OverflowError(f"{value} does not fit a C int")
+        return ctypes.c_int(value)
+
+
+class _Size(ctypes.c_size_t):
+    """size_t argument that rejects negative and oversized values instead of wrapping."""
+
+    @classmethod
+    def from_param(cls, value):
+        value = operator.index(value)
+        if not 0 <= value < (1 << (8 * ctypes.sizeof(ctypes.c_size_t))):
+            raise OverflowError(f"{value} does not fit a C size_t")
+        return ctypes.c_size_t(value)
+
+
 def _declare(lib):
-    vp, i, f, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    vp, i, f, sz = ctypes.c_void_p, _Int32, ctypes.c_float, _Size
     lib.fa_fwd.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
-    lib.fa_fwd.restype = i
+    lib.fa_fwd.restype = ctypes.c_int
     lib.fa_fwd_workspace_bytes.argtypes = [i, i, i, i]
-    lib.fa_fwd_workspace_bytes.restype = sz
+    lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_fwd_ws.restype = i
+    lib.fa_fwd_ws.restype = ctypes.c_int
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp]
-    lib.fa_fwd_fp8.restype = i
+    lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8_ws.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_fwd_fp8_ws.restype = i
+    lib.fa_fwd_fp8_ws.restype = ctypes.c_int
     lib.fa_decode_workspace_bytes.argtypes = [i, i, i, i, i]
-    lib.fa_decode_workspace_bytes.restype = sz
+    lib.fa_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_decode.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_decode.restype = i
+    lib.fa_decode.restype = ctypes.c_int
     lib.fa_decode_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_decode_varlen.restype = i
+    lib.fa_decode_varlen.restype = ctypes.c_int
     lib.fa_bwd_workspace_bytes.argtypes = [i, i, i, i]
-    lib.fa_bwd_workspace_bytes.restype = sz
+    lib.fa_bwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
-    lib.fa_bwd.restype = i
+    lib.fa_bwd.restype = ctypes.c_int
     lib.fa_status_string.argtypes = [i]
     lib.fa_status_string.restype = ctypes.c_char_p
     return lib

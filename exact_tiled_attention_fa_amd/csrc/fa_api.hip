@@ -24,6 +24,11 @@ int64_t elems(int64_t B, int64_t H, int64_t N, int64_t d) {
   return x;
 }
 
+// Longest sequence (N or L) accepted: keeps every in-head index expression of
+// the kernels and planners (a row or key plus one block, L + num_splits - 1)
+// inside int. One head's Q at that length and d = 64 is already 128 GiB.
+constexpr int kMaxSeq = 1 << 30;
+
 int decode_chunk(int L, int num_splits) { return (L + num_splits - 1) / num_splits; }
 int decode_splits_used(int L, int num_splits) {
   const int chunk = decode_chunk(L, num_splits);
@@ -91,7 +96,7 @@ int check_fwd_args(const void* q, const void* k, const void* v, const void* o, c
 // split, which targets at most two per CU beyond it) and the combine's
 // one-wave-per-row grid must fit a launch.
 int check_fwd_sizes(int B, int Hq, int N, int d) {
-  if (B <= 0 || Hq <= 0 || N <= 0 || (d != 64 && d != 128)) return FA_ERR_SHAPE;
+  if (B <= 0 || Hq <= 0 || N <= 0 || N > kMaxSeq || (d != 64 && d != 128)) return FA_ERR_SHAPE;
   if (elems(B, Hq, N, d) < 0) return FA_ERR_SHAPE;
   const int64_t nqb = (N + fa::kFwdWaveRows * 4 - 1) / (fa::kFwdWaveRows * 4);  // the smaller blocks
   if ((int64_t)B * Hq * nqb > INT32_MAX / 4 || (int64_t)B * Hq * N > INT32_MAX) return FA_ERR_SHAPE;
@@ -335,7 +340,8 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
 }
 
 extern "C" size_t fa_decode_workspace_bytes(int B, int Hq, int L, int d, int num_splits) {
-  if (B <= 0 || Hq <= 0 || L <= 0 || (d != 64 && d != 128) || num_splits < 1 || num_splits > L) return 0;
+  if (B <= 0 || Hq <= 0 || L <= 0 || L > kMaxSeq || (d != 64 && d != 128) || num_splits < 1 || num_splits > L)
+    return 0;
   const int S = decode_splits_used(L, num_splits);
   const int64_t rows = (int64_t)B * Hq;
   const int64_t floats = rows * S * (int64_t)d + rows * S;
@@ -349,7 +355,7 @@ int decode_impl(const void* q, const void* k, const void* v, void* o, float* lse
                 int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
                 void* workspace, size_t workspace_bytes, fa_stream_t stream) {
   if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
-  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0) return FA_ERR_SHAPE;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || L <= 0 || L > kMaxSeq) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_HEAD_DIM;
   if (Hq % Hkv != 0) return FA_ERR_GQA;
   if (num_splits < 1 || num_splits > L) return FA_ERR_SHAPE;

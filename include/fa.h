@@ -47,7 +47,8 @@ typedef struct ihipStream_t* fa_stream_t;
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL = -1,      /* a required pointer is NULL */
-  FA_ERR_SHAPE = -2,     /* a size is <= 0, too large, or num_splits out of range */
+  FA_ERR_SHAPE = -2,     /* a size is <= 0, too large (N or L above 2^30, B*Hq*N above 2^31 - 1,
+                            a grid beyond 2^31 - 1 work-groups), or num_splits out of range */
   FA_ERR_HEAD_DIM = -3,  /* d is not 64 or 128 */
   FA_ERR_GQA = -4,       /* Hq is not a multiple of Hkv */
   FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */

@@ -61,6 +61,7 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0
     (dict(q=BAD), -5), (dict(o=BAD), -5), (dict(lse=P + 2), -5),
     (dict(causal=2), -8), (dict(scale=float("nan")), -8), (dict(scale=float("inf")), -8),
     (dict(B=1 << 20, Hq=1 << 12, N=1 << 20), -2),
+    (dict(N=(1 << 30) + 1), -2), (dict(N=(1 << 31) - 1), -2),
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
@@ -83,6 +84,7 @@ def test_fwd_workspace_size_rules(lib):
     assert lib.fa_fwd_workspace_bytes(0, 1, 128, 128) == 0
     assert lib.fa_fwd_workspace_bytes(1, 1, 128, 96) == 0
     assert lib.fa_fwd_workspace_bytes(1, 1, 960, 128) == 0  # 15 key tiles: never split
+    assert lib.fa_fwd_workspace_bytes(1, 1, (1 << 31) - 1, 64) == 0
 
 
 def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4, scale=0.1, ws=P, wsb=1 << 30):
@@ -96,6 +98,7 @@ def dec(lib, q=P, k=P, v=P, o=P, lse=P, B=2, Hq=8, Hkv=2, L=100, d=128, splits=4
     (dict(k=BAD), -5), (dict(ws=BAD), -5),
     (dict(scale=float("nan")), -8),
     (dict(ws=None), -6), (dict(wsb=16), -6),
+    (dict(L=(1 << 31) - 1, splits=(1 << 31) - 1), -2), (dict(L=(1 << 30) + 1, splits=1), -2),
 ])
 def test_decode_rejects(lib, kw, status):
     assert dec(lib, **kw) == status
@@ -126,6 +129,7 @@ def bwd(lib, q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, Hq=2, Hkv=1
     (dict(N=0), -2), (dict(B=-1), -2), (dict(d=256), -3), (dict(d=96), -3), (dict(Hq=3, Hkv=2), -4),
     (dict(dv=BAD), -5), (dict(do=BAD), -5), (dict(ws=BAD), -5), (dict(causal=3), -8),
     (dict(scale=float("nan")), -8), (dict(ws=None), -6), (dict(wsb=64), -6),
+    (dict(N=(1 << 30) + 1), -2),
 ])
 def test_bwd_rejects(lib, kw, status):
     assert bwd(lib, **kw) == status
@@ -146,6 +150,7 @@ def test_decode_workspace_size(lib):
     assert lib.fa_decode_workspace_bytes(1, 1, 5, 64, 4) == (3 * 65 * 4 + 255) // 256 * 256
     assert lib.fa_decode_workspace_bytes(1, 1, 5, 64, 6) == 0
     assert lib.fa_decode_workspace_bytes(1, 1, 5, 60, 1) == 0
+    assert lib.fa_decode_workspace_bytes(1, 1, (1 << 31) - 1, 64, (1 << 31) - 1) == 0
 
 
 def test_binding_refuses_cpu_tensors():
@@ -187,6 +192,20 @@ def test_fwd_fp8_ws_rejects(lib):
     assert call(q=None) == -1
     assert call(d=96) == -3
     assert call(vs=float("nan")) == -8
+
+
+def test_binding_refuses_ints_that_do_not_fit(lib):
+    # ctypes would keep the low 32 bits of 2**32 + 128 (i.e. 128); the loader raises instead.
+    # Each call also carries a NULL q, so none could reach a launch.
+    with pytest.raises(ctypes.ArgumentError):
+        lib.fa_fwd_workspace_bytes(1, 1, (1 << 32) + 128, 128)
+    with pytest.raises(ctypes.ArgumentError):
+        lib.fa_decode_workspace_bytes(1, 1, 100, 128, -(1 << 31) - 1)
+    with pytest.raises(ctypes.ArgumentError):
+        lib.fa_fwd_workspace_bytes(1, 1, 128.0, 128)
+    with pytest.raises(ctypes.ArgumentError):  # negative size_t would wrap to a huge workspace
+        lib.fa_fwd_ws(None, P, P, P, P, 1, 1, 1, 128, 128, 0, 0.1, P, -1, None)
+    assert fwd_ws(lib, q=None, wsb=(1 << 64) - 1) == -1
 
 
 def test_missing_library_raises(monkeypatch):
