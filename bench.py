@@ -15,6 +15,9 @@ kernel, plus the combine kernel when the keys are split). The decode rate is
 reported as algorithmic HBM GB/s (K and V read once per KV head). The "also"
 section adds other workloads and, for the step's three calls, cold-cache
 timings (median and minimum of 50 single calls, each after reading 1 GiB).
+"rocprof_counters" repeats, per workload, the committed rocprofv3 counter
+figures (HBM-side bytes over the Q+K+V+O floor, L2 hit rate, MFMA busy, clock)
+while the library's sources are the ones they were taken from, else null.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --calibrate-copy   (plain copy kernel of known size, for
@@ -73,6 +76,44 @@ def measured_traffic():
         return float(fields["hbm_bytes_per_launch"])
     except (KeyError, ValueError):
         return None
+
+
+ALL_COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_decode_counters_by_workload.md")
+
+
+def all_sources_hash() -> str:
+    """Digest of every kernel and host source of the library (csrc/*.hip, *.h, sorted by name)."""
+    d = os.path.join(ROOT, "exact_tiled_attention_fa_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".h")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_counters():
+    """Per-workload rocprofv3 figures (HBM-side bytes over the floor, L2 hit rate, MFMA busy, clock) from the
+    committed counter summary, or None when it is missing or was taken from other sources."""
+    if not os.path.exists(ALL_COUNTERS_FILE):
+        return None
+    recs, digest = {}, None
+    for line in open(ALL_COUNTERS_FILE):
+        t = line.strip()
+        if t.startswith("sources_sha256_16:"):
+            digest = t.split(":", 1)[1].strip()
+        elif t.startswith("{") and '"workload"' in t:
+            r = json.loads(t)
+            out = {"bytes_over_floor": r["bytes_over_floor"], "call_bytes": r["call_bytes"],
+                   "floor_bytes": r["floor_bytes"]}
+            k0 = next(iter(r["kernels"].values()))  # the call's main kernel
+            for f in ("l2_hit", "mfma_util_counted", "mfma_busy_est", "clock_ghz_est"):
+                if f in k0:
+                    out[f] = k0[f]
+            recs[r["workload"]] = out
+    if digest != all_sources_hash() or not recs:
+        return None
+    return recs
 
 
 SETTLE_S = 0.5
@@ -416,6 +457,7 @@ def main() -> int:
         "decode_frac_hbm_peak": round(dec_gbs / PEAK_HBM_GBS, 4),
         "decode_us": round(t_dec * 1e6, 2),
         "also": extra,
+        "rocprof_counters": measured_counters(),
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(fcase, args.cpu_seconds)
