@@ -508,17 +508,27 @@ void fa_fwd_kernel(FwdArgs a) {
 
 // Merge each row's non-empty key splits with the log-sum-exp combine; D / 8
 // lanes take one row, eight columns each, so every partial of a row is one
-// 16-byte load per lane.
+// 16-byte load per lane. The work-groups take the query blocks in the forward
+// grid's order (without its key-split level) through the same XCD-contiguous
+// mapping, a block's rows in a.rows / RPG consecutive work-groups: each XCD
+// then merges the blocks whose partials its own forward work-groups wrote.
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kMergeThreads) void fa_fwd_combine_kernel(FwdArgs a) {
   constexpr int LPR = D / 8;                 // lanes per row
   constexpr int RPG = kMergeThreads / LPR;   // rows per work-group
-  const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t row = (size_t)blockIdx.x * RPG + threadIdx.x / LPR;
-  if (row >= rows) return;
+  const int chunks = a.rows / RPG;           // work-groups per query block
+  const int lid = xcd_contiguous(blockIdx.x, a.B * a.Hq * a.nqb * chunks);
+  const int blk = lid / chunks;
+  const int grp = blk / (a.head_group * a.nqb);
+  const int rem_g = blk - grp * a.head_group * a.nqb;
+  const int gh = min(a.head_group, a.B * a.Hq - grp * a.head_group);
+  const int qs = rem_g / gh;
+  const int bh = grp * a.head_group + (rem_g - qs * gh);
+  const int qb = CAUSAL ? a.nqb - 1 - qs : qs;
+  const int n = qb * a.rows + (lid - blk * chunks) * RPG + (int)threadIdx.x / LPR;
+  if (n >= a.N) return;
+  const size_t row = (size_t)bh * a.N + n;
   const int col = 8 * (threadIdx.x % LPR);
-  const int n = (int)(row % (size_t)a.N);
-  const int qb = n / a.rows;
   const int kv_end = CAUSAL ? min(a.N, qb * a.rows + a.rows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
   const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
@@ -543,12 +553,15 @@ hipError_t launch_fwd(const FwdArgs& a, int d, bool causal, hipStream_t stream) 
   return d == 128 ? launch_fwd_d<128>(a, causal, stream) : launch_fwd_d<64>(a, causal, stream);
 }
 
+// One work-group per (query block, RPG-row chunk of it). Key splits are only
+// planned for grids of fewer query blocks than twice the CU count, so the
+// grid stays far below the int range the kernel indexes it with.
 template <int D, bool CAUSAL>
 static hipError_t launch_combine_t(const FwdArgs& a, hipStream_t stream) {
-  const size_t rows = (size_t)a.B * a.Hq * a.N;
-  const size_t per_wg = kMergeThreads / (D / 8);
-  hipLaunchKernelGGL((fa_fwd_combine_kernel<D, CAUSAL>), dim3((unsigned)((rows + per_wg - 1) / per_wg)),
-                     dim3(kMergeThreads), 0, stream, a);
+  const int chunks = a.rows / (kMergeThreads / (D / 8));
+  const size_t nwg = (size_t)a.B * a.Hq * a.nqb * chunks;
+  if (a.rows % (kMergeThreads / (D / 8)) != 0 || nwg > (size_t)INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((fa_fwd_combine_kernel<D, CAUSAL>), dim3((unsigned)nwg), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 
