@@ -15,6 +15,9 @@ kernel, plus the combine kernel when the keys are split). The decode rate is
 reported as algorithmic HBM GB/s (K and V read once per KV head). The "also"
 section adds other workloads and, for the step's three calls, cold-cache
 timings (median and minimum of 50 single calls, each after reading 1 GiB).
+"cpu_baseline" also carries "seconds_by_config": the oracle's time per
+workload config over the rows its parity checks use (one head or sequence
+timed, scaled by their count; all-rows times of sampled configs extrapolated).
 "rocprof_counters" repeats, per workload, the committed rocprofv3 counter
 figures (HBM-side bytes over the Q+K+V+O floor, L2 hit rate, MFMA busy, clock)
 while the library's sources are the ones they were taken from, else null.
@@ -235,7 +238,51 @@ def cpu_baseline(case, seconds: float) -> dict:
     flops = passes * 4.0 * case.N * case.N * case.d
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{passes} full pass(es) of the 1x1x8192 d128 non-causal forward ({rows_total} rows) "
-                      f"in {dt:.1f} s, FP64 NumPy three-pass attention"}
+                      f"in {dt:.1f} s, FP64 NumPy three-pass attention",
+            "seconds_by_config": oracle_seconds_by_config()}
+
+
+def oracle_seconds_by_config(cases=None, decode_cases=None) -> dict:
+    """Seconds the FP64 oracle takes per workload config, over the rows its parity checks use.
+
+    The oracle treats heads (and decode sequences) independently, so each config is timed on one
+    head (one sequence) of seeded N(0,1) inputs of its shape and scaled by the head (sequence) count;
+    large configs use the parity tests' seeded sample of rows per head, with the time for every
+    row extrapolated linearly (the oracle scores every key of a row, masked or not)."""
+    import dataclasses
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import fa_oracle
+    if cases is None:
+        cases = (si.TINY, si.ONE_HEAD_8K, si.ONE_HEAD_8K_CAUSAL, si.HEADS32_4K, si.HEADS32_4K_CAUSAL, si.LONG_128K)
+    if decode_cases is None:
+        decode_cases = (si.DECODE_GQA,)
+    out = {}
+    for case in cases:
+        one = dataclasses.replace(case, B=1, Hq=1, Hkv=1)
+        q, k, v = (si.bf16_bits_to_f32(x) for x in si.fwd_inputs(one))
+        rows = None
+        if case.sampled_rows and case.sampled_rows < case.N:
+            rows = si.sample_rows(case.seed, 0, case.N, case.sampled_rows)
+        t0 = time.perf_counter()
+        fa_oracle.attention_ref(q, k, v, case.causal, case.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        heads = case.B * case.Hq
+        rec = {"seconds_one_head": round(dt, 3), "rows_per_head": case.N if rows is None else len(rows),
+               "heads": heads, "seconds": round(dt * heads, 3)}
+        if rows is not None:
+            rec["seconds_all_rows_extrapolated"] = round(dt * heads * case.N / len(rows), 1)
+        out[case.name] = rec
+        del q, k, v
+    for case in decode_cases:
+        one = dataclasses.replace(case, B=1)
+        q, k, v = (si.bf16_bits_to_f32(x) for x in si.decode_inputs(one))
+        t0 = time.perf_counter()
+        fa_oracle.decode_ref(q, k, v, case.scale)
+        dt = time.perf_counter() - t0
+        out[case.name] = {"seconds_one_sequence": round(dt, 3), "sequences": case.B, "rows": case.B * case.Hq,
+                          "seconds": round(dt * case.B, 3)}
+    return out
 
 
 def main() -> int:

@@ -63,3 +63,18 @@ def test_committed_counter_summary_is_consistent():
         assert r["bytes_over_floor"] == pytest.approx(r["call_bytes"] / r["floor_bytes"], abs=1e-3)
         for k in r["kernels"].values():
             assert 0 <= k["l2_hit"] <= 1 and 0 <= k["mfma_util_counted"] <= 1
+
+
+def test_oracle_seconds_by_config_scales_one_head():
+    import dataclasses
+    import seeded_inputs as si
+    fwd = dataclasses.replace(si.TINY, name="tiny 3 heads", B=1, Hq=3, Hkv=3, N=256, sampled_rows=64)
+    dec = si.DecodeCase("tiny decode", 2, 4, 2, 64, 64, 4, seed=1)
+    r = bench.oracle_seconds_by_config(cases=(fwd,), decode_cases=(dec,))
+    f = r["tiny 3 heads"]
+    assert f["heads"] == 3 and f["rows_per_head"] == 64
+    assert f["seconds"] == pytest.approx(3 * f["seconds_one_head"], abs=2e-3)
+    assert f["seconds_all_rows_extrapolated"] == pytest.approx(f["seconds"] * 4, abs=0.1)
+    d = r["tiny decode"]
+    assert d["sequences"] == 2 and d["rows"] == 8
+    assert d["seconds"] == pytest.approx(2 * d["seconds_one_sequence"], abs=2e-3)
