@@ -27,6 +27,23 @@ def _stream_handle(device: torch.device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
+def _one_device(*named) -> torch.device:
+    """The one GPU that every given tensor lives on: the kernels run there and
+    read or write all of them, so a tensor elsewhere (another GPU, host
+    memory) is refused before any launch. None entries are skipped."""
+    dev = None
+    for name, t in named:
+        if t is None:
+            continue
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError(f"{name} is on {t.device} but the other tensors are on {dev}: all must share one GPU")
+    return dev
+
+
 def _check_bf16(name: str, t: torch.Tensor, ndim: int) -> None:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
@@ -61,8 +78,10 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("out must match q's shape")
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
-    st = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                           B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(q.device))
+    dev = _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
+    with torch.cuda.device(dev):
+        st = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                               B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(dev))
     _lib.check(st, "fa_fwd")
     return out, lse
 
@@ -85,6 +104,7 @@ def _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale):
         raise ValueError("out must match q's shape")
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return (q.data_ptr(), k.data_ptr(), v.data_ptr(), float(q_scale), float(k_scale), float(v_scale),
@@ -102,8 +122,9 @@ def fwd_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, q_scale: float, k
         out = torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     if lse is None:
         lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
-    st = _lib.lib().fa_fwd_fp8(*_fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale),
-                               _stream_handle(q.device))
+    args = _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale)
+    with torch.cuda.device(q.device):
+        st = _lib.lib().fa_fwd_fp8(*args, _stream_handle(q.device))
     _lib.check(st, "fa_fwd_fp8")
     return out, lse
 
@@ -113,14 +134,16 @@ def prepare_fwd_fp8(q, k, v, q_scale, k_scale, v_scale, out, lse, causal: bool =
     """Like prepare_fwd, for fwd_fp8 (one fa_fwd_fp8_ws call per invocation)."""
     args = _fp8_args(q, k, v, q_scale, k_scale, v_scale, out, lse, causal, scale)
     B, Hq, N, d = q.shape
-    need = fwd_workspace_bytes(B, Hq, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    device = q.device
+    with torch.cuda.device(device):
+        need = fwd_workspace_bytes(B, Hq, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
     fn = _lib.lib().fa_fwd_fp8_ws
     tail = (ws.data_ptr() if ws is not None else None, need)
-    device = q.device
 
     def call():
-        st = fn(*args, *tail, torch.cuda.current_stream(device).cuda_stream)
+        with torch.cuda.device(device):
+            st = fn(*args, *tail, torch.cuda.current_stream(device).cuda_stream)
         if st:
             _lib.check(st, "fa_fwd_fp8_ws")
     call.workspace = ws
@@ -134,6 +157,12 @@ def fwd_workspace_bytes(B: int, Hq: int, N: int, d: int) -> int:
 
 def decode_workspace_bytes(B: int, Hq: int, L: int, d: int, num_splits: int) -> int:
     return int(_lib.lib().fa_decode_workspace_bytes(B, Hq, L, d, num_splits))
+
+
+def _check_workspace(ws) -> None:
+    """A caller's workspace is handed over as (pointer, bytes): it must be one contiguous block."""
+    if not isinstance(ws, torch.Tensor) or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous GPU tensor")
 
 
 def _check_lens(seq_lens: torch.Tensor, B: int, device) -> None:
@@ -170,6 +199,19 @@ def decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, num_splits: int = 
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device)
+    _check_bf16("out", out, 4)
+    if out.shape != q.shape:
+        raise ValueError("out must match q's shape [B,Hq,1,d]")
+    if lse.dtype != torch.float32 or lse.shape != (B, Hq) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
+    _check_workspace(workspace)
+    _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("workspace", workspace),
+                ("seq_lens", seq_lens))
+    with torch.cuda.device(q.device):
+        return _decode_call(q, k, v, out, lse, workspace, seq_lens, B, Hq, Hkv, L, d, num_splits, scale)
+
+
+def _decode_call(q, k, v, out, lse, workspace, seq_lens, B, Hq, Hkv, L, d, num_splits, scale):
     if seq_lens is None:
         st = _lib.lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
                                   B, Hq, Hkv, L, d, num_splits, float(scale), workspace.data_ptr(),
@@ -200,6 +242,9 @@ def _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace):
         raise ValueError("o, dout, dq must be [B,Hq,N,d]")
     if lse.dtype != torch.float32 or lse.shape != (B, Hq, N) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
+    _check_workspace(workspace)
+    _one_device(("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("dout", dout), ("dq", dq), ("dk", dk),
+                ("dv", dv), ("workspace", workspace))
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     return (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(), dout.data_ptr(),
@@ -216,8 +261,9 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, lse:
     if workspace is None:
         workspace = torch.empty(max(bwd_workspace_bytes(B, Hq, N, d), 16), dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    st = _lib.lib().fa_bwd(*_bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace),
-                           _stream_handle(q.device))
+    args = _bwd_args(q, k, v, o, lse, dout, dq, dk, dv, causal, scale, workspace)
+    with torch.cuda.device(q.device):
+        st = _lib.lib().fa_bwd(*args, _stream_handle(q.device))
     _lib.check(st, "fa_bwd")
     return dq, dk, dv
 
@@ -229,7 +275,8 @@ def prepare_bwd(q, k, v, o, lse, dout, dq, dk, dv, workspace, causal: bool = Fal
     device = q.device
 
     def call():
-        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        with torch.cuda.device(device):
+            st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
         if st:
             _lib.check(st, "fa_bwd")
     return call
@@ -253,15 +300,17 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    device = _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     fn = _lib.lib().fa_fwd_ws
-    need = fwd_workspace_bytes(B, Hq, N, d)
-    ws = torch.empty(need, dtype=torch.uint8, device=q.device) if need else None
+    with torch.cuda.device(device):
+        need = fwd_workspace_bytes(B, Hq, N, d)
+    ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), ws.data_ptr() if ws is not None else None, need)
-    device = q.device
 
     def call():
-        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        with torch.cuda.device(device):
+            st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
         if st:
             _lib.check(st, "fa_fwd_ws")
     call.workspace = ws  # keeps the buffer alive with the callable
@@ -283,6 +332,9 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
         raise ValueError("lse must be a contiguous float32 [B,Hq] tensor")
     if scale is None:
         scale = 1.0 / math.sqrt(d)
+    _check_workspace(workspace)
+    _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse), ("workspace", workspace),
+                ("seq_lens", seq_lens))
     if seq_lens is None:
         fn, name = _lib.lib().fa_decode, "fa_decode"
         head = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr())
@@ -295,7 +347,8 @@ def prepare_decode(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch
     device = q.device
 
     def call():
-        st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+        with torch.cuda.device(device):
+            st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
         if st:
             _lib.check(st, name)
     return call

@@ -161,6 +161,22 @@ def test_binding_refuses_cpu_tensors():
         fa.fwd(x, x, x)
 
 
+def test_binding_requires_one_gpu_for_every_tensor():
+    """A tensor on another GPU or in host memory (lse, workspace, seq_lens included) is refused before any call."""
+    torch = pytest.importorskip("torch")
+    from types import SimpleNamespace
+    import exact_tiled_attention_fa_amd as fa
+    g0, g1 = SimpleNamespace(device=torch.device("cuda:0")), SimpleNamespace(device=torch.device("cuda:1"))
+    host = SimpleNamespace(device=torch.device("cpu"))
+    assert fa._one_device(("q", g0), ("k", g0), ("seq_lens", None)) == torch.device("cuda:0")
+    with pytest.raises(ValueError, match="k is on cuda:1"):
+        fa._one_device(("q", g0), ("k", g1))
+    with pytest.raises(ValueError, match="lse must be on a GPU"):
+        fa._one_device(("q", g0), ("lse", host))
+    with pytest.raises(ValueError, match="contiguous"):
+        fa._check_workspace(torch.zeros(64, dtype=torch.uint8)[::2])
+
+
 def fwd_fp8(lib, q=P, k=P, v=P, qs=0.01, ks=0.01, vs=0.01, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128,
             causal=0, scale=0.125):
     return lib.fa_fwd_fp8(q, k, v, qs, ks, vs, o, lse, B, Hq, Hkv, N, d, causal, scale, None)
