@@ -18,10 +18,16 @@
  * Conventions shared by every entry point:
  *   - Tensor pointers are DEVICE pointers owned by the caller. The library never
  *     frees them and keeps no reference after the call returns.
+ *   - Every tensor of a call, its workspace and `stream` belong to one GPU, which
+ *     must be the calling thread's current HIP device: launch planning (key
+ *     splits, workspace sizes) reads that device's compute-unit count, and
+ *     fa_fwd's temporary buffer comes from its memory pool.
  *   - BF16 tensors are IEEE bfloat16 bit patterns; every tensor is contiguous
  *     (row-major in the order its shape is written) and 16-byte aligned.
- *   - Argument checks run on the host before any HIP call. On failure the call
- *     returns a negative fa_status and launches nothing; outputs are untouched.
+ *   - Argument checks run on the host before any launch or allocation (the
+ *     only HIP call before them is a cached compute-unit-count query). On
+ *     failure the call returns a negative fa_status and launches nothing;
+ *     outputs are untouched.
  *   - Work is enqueued asynchronously on `stream` (NULL = the null stream). A
  *     launch failure returns FA_ERR_LAUNCH; faults during execution surface at
  *     the caller's next synchronisation.
