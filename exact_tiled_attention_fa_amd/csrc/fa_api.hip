@@ -113,9 +113,9 @@ struct FwdPlan {
 // Key split for grids that would leave CUs idle: aim at as many work-groups
 // as fit on the CUs at once (one of 8 waves or two of 4 per CU), never fewer
 // than kMinSplitTiles key tiles per split.
-FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal) {
+FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal, bool fp8) {
   FwdPlan p;
-  const int waves = fa::fwd_waves(causal, N, (int64_t)B * Hq * ((N + 255) / 256), device_cu_count());
+  const int waves = fa::fwd_waves(causal, N, (int64_t)B * Hq * ((N + 255) / 256), device_cu_count(), fp8);
   p.rows = fa::kFwdWaveRows * waves;
   // Causal blocks differ in work (heaviest first). Each of the 8 XCDs takes a
   // contiguous range of the grid; when that range is a whole number (>= 2) of
@@ -172,9 +172,14 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
 
 extern "C" size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d) {
   if (check_fwd_sizes(B, Hq, N, d) != FA_OK) return 0;
-  // Enough for either mask (the plan depends on it).
-  const size_t a = plan_fwd(B, Hq, N, d, false).ws_bytes, c = plan_fwd(B, Hq, N, d, true).ws_bytes;
-  return a > c ? a : c;
+  // Enough for either mask and either input type (the plan depends on both).
+  size_t most = 0;
+  for (int causal = 0; causal < 2; ++causal)
+    for (int fp8 = 0; fp8 < 2; ++fp8) {
+      const size_t b = plan_fwd(B, Hq, N, d, causal != 0, fp8 != 0).ws_bytes;
+      if (b > most) most = b;
+    }
+  return most;
 }
 
 extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
@@ -183,7 +188,7 @@ extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, f
   int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
   if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, false);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -198,7 +203,7 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
   if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, false);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.ws_bytes == 0) return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, nullptr, s);
   void* ws = nullptr;
@@ -254,7 +259,7 @@ extern "C" int fa_fwd_fp8_ws(const void* q, const void* k, const void* v, float 
                              fa_stream_t stream) {
   const int st = check_fp8_args(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, true);
   if (p.ws_bytes > 0) {
     if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
@@ -268,7 +273,7 @@ extern "C" int fa_fwd_fp8(const void* q, const void* k, const void* v, float q_s
                           float scale, fa_stream_t stream) {
   int st = check_fp8_args(q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale);
   if (st != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0);
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, true);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   if (p.ws_bytes == 0)
     return launch_fwd_fp8_planned(p, q, k, v, q_scale, k_scale, v_scale, o, lse, B, Hq, Hkv, N, d, causal, scale,

@@ -42,11 +42,15 @@ constexpr int kFwdWaveRows = 32;  // query rows per wave
 // diagonal (every wave of a block takes every tile of the block) and balance
 // the short, unequal blocks better; also 4 for causal sweeps shorter than 16K
 // whose 256-row blocks would not fill the CUs (the key-split path).
-// Measured on 32 x 4K, 16 x 8K and 8 x 16K causal heads: 4 waves win by 11% at
-// 4K, 8 waves by 6.5% and 8% above; one 8K head (split) is 1% faster with 4.
-inline int fwd_waves(bool causal, int N, int64_t blocks256, int cus) {
+// One exception in BF16: from 4K keys, when the 256-row blocks make exactly two
+// per CU, the heaviest-first order hands every CU that frees up the heaviest
+// block left, so each CU's two blocks add up to about the same work and 8
+// waves win (32 causal heads at 4K: 137.7 -> 131.8 us at d = 128, 85.4 -> 81.6
+// at d = 64; with one, three or four blocks per CU 8 waves lose 1-15%, and the
+// FP8 pass loses 1-3% at two).
+inline int fwd_waves(bool causal, int N, int64_t blocks256, int cus, bool fp8) {
   if (!causal) return 8;
-  if (N < 8192) return 4;
+  if (N < 8192) return !fp8 && N >= 4096 && blocks256 == 2 * (int64_t)cus ? 8 : 4;
   return N < 16384 && blocks256 < cus ? 4 : 8;
 }
 
