@@ -74,6 +74,14 @@ def test_causal_8k_many_heads():
     _run_case(si.FwdCase("1x8x8192 d128 causal", 1, 8, 8, 8192, 128, True, seed=41, sampled_rows=256))
 
 
+@pytest.mark.parametrize("Hkv,d", [(32, 64), (8, 128)])
+def test_causal_two_blocks_per_cu(Hkv, d):
+    """32 causal heads of 4K: on a 256-CU part their 256-row blocks make exactly two per CU, which the
+    BF16 planner runs as 8-wave blocks (heads interleaved per XCD, heaviest first); d = 64, and GQA."""
+    _run_case(si.FwdCase(f"1x32x4096 d{d} causal kv{Hkv}", 1, 32, Hkv, 4096, d, True, seed=60 + d + Hkv,
+                         sampled_rows=256))
+
+
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 24, 24, 300, 64), (2, 8, 4, 500, 128), (1, 16, 2, 190, 128)])
 def test_causal_head_groups(B, Hq, Hkv, N, d):
     """Causal grids whose B*Hq is a multiple of 8 (>= 16) interleave the blocks
