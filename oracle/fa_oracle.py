@@ -34,8 +34,6 @@ inputs and torch's FP64 CPU scaled_dot_product_attention).
 """
 from __future__ import annotations
 
-import math
-
 import numpy as np
 
 ROW_CHUNK = 256  # rows per materialised S block (bounds memory to 256 x N x 8 B)
@@ -175,14 +173,6 @@ def attention_bwd_ref(q, k, v, do, causal: bool, scale: float, rows=None, key_ro
     return dq_out, dk_out, dv_out
 
 
-def bwd_flops(N: int, d: int, causal: bool, heads: int = 1) -> float:
-    """Algorithmic backward FLOPs: five N x N x d products (S, dV, dP, dQ, dK),
-    10 N^2 d per head, halved for causal (the usual count; recomputation of S
-    is included, extra recomputation by an implementation is not)."""
-    f = 10.0 * N * N * d * heads
-    return f / 2 if causal else f
-
-
 def decode_ref(q, k, v, scale: float):
     """One query token per (sequence, query head) against the whole KV cache.
 
@@ -319,18 +309,3 @@ def attention_fp8_ref(q8, k8, v8, q_scale: float, k_scale: float, v_scale: float
     k = fp8_e4m3_value(k8) * float(k_scale)
     v = fp8_e4m3_value(v8) * float(v_scale)
     return attention_ref(q, k, v, causal, scale, rows=rows, return_p=return_p)
-
-
-def fwd_flops(N: int, d: int, causal: bool, heads: int = 1) -> float:
-    """Algorithmic forward FLOPs: 4 N^2 d per head (QK^T and PV), halved for causal.
-
-    "FlashAttention HBM bytes, one head, 8K": FLOPs = 4 N^2 d (A strong answer)
-    and halved when causal (What interviewers probe next).
-    """
-    f = 4.0 * N * N * d * heads
-    return f / 2 if causal else f
-
-
-def time_budget_rows(N: int, d: int, target_flops: float) -> int:
-    """How many query rows of an N-key head cost about ``target_flops`` here."""
-    return max(1, int(math.floor(target_flops / (4.0 * N * d))))
