@@ -66,21 +66,26 @@ __device__ __forceinline__ int sw2(int r) {
 template <int D>
 __device__ __forceinline__ int swr(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
-// Direct loads of a 64-row tile of a row-major [rows, D] BF16 matrix into
-// LDS: wave w fills the 1 KiB blocks BPW w .. BPW w + BPW - 1; lane l writes
-// physical chunk l % CPR of its row with logical chunk (l % CPR) ^ sw.
-// Rows past `rows` read the last row (finite data the caller masks).
+// Direct loads of the 64-row tile starting at row row0 of a row-major
+// [rows, D] BF16 matrix into LDS: wave w fills the 1 KiB blocks
+// BPW w .. BPW w + BPW - 1; lane l writes physical chunk l % CPR of its row
+// with logical chunk (l % CPR) ^ sw. The base moves to the tile's first row in
+// 64-bit arithmetic, so each lane's 32-bit byte offset spans one tile (at most
+// 16 KiB) whatever the sequence length. Rows past `rows` read the last row
+// (finite data the caller masks).
 template <int D, bool SW2>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int rows, uint4* dst, int wave, int lane) {
   using C = BwdCfg<D>;
   const int pc = lane % C::CPR;
   const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(C::BPW * wave);
+  const uint16_t* base = src + (size_t)row0 * D;
+  const int last = rows - 1 - row0;  // >= 0: a tile starts below `rows`
 #pragma unroll
   for (int x = 0; x < C::BPW; ++x) {
     const int r = C::RPB * (C::BPW * wave + x) + lane / C::CPR;
     const int sw = SW2 ? sw2<D>(r) : swr<D>(r);
-    const int row = min(row0 + r, rows - 1);
-    dma16(src, 2u * (uint32_t)(row * D + 8 * (pc ^ sw)), l0 + 1024u * x);
+    const int row = min(r, last);
+    dma16(base, 2u * (uint32_t)(row * D + 8 * (pc ^ sw)), l0 + 1024u * x);
   }
 }
 

@@ -4,7 +4,7 @@ The GPU runs its own forward (o, lse), then the backward from those and a
 seeded upstream gradient; the oracle differentiates the exact attention of the
 same BF16-valued inputs. Small cases are gated element-wise by a bound derived
 from the kernels' arithmetic (gpu_helpers.bwd_elem_bounds); the 32-head 4K
-workload is checked on two heads' sampled rows and keys by a normwise gate.
+workload is checked on eight heads' sampled rows and keys by the same bound.
 """
 import sys
 
@@ -82,27 +82,23 @@ def test_bwd_scale_edge_cases_d64(scale):
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_bwd_32_heads_4k_sampled(causal):
-    """The 32-head 4K shape (the bench's backward workload), all heads on the GPU;
-    heads 0 and 31 compared on 1,024 seeded rows (dQ) and keys (dK, dV)."""
+    """The 32-head 4K shape (the bench's backward workload), all heads on the GPU.
+    Eight heads, at least one in each XCD's range of the grid (four heads per
+    XCD without causal masking; causal grids interleave the heads of a range),
+    are compared on 1,024 seeded rows (dQ) and keys (dK, dV) with the derived
+    element-wise bounds of the small cases."""
     B, Hq, N = 1, 32, 4096
     qb, kb, vb, gb = _inputs(B, Hq, Hq, N, seed=3)
     scale = 128 ** -0.5
-    print(f"[bwd] 1x32x4096 causal={causal} (heads 0, 31 sampled)", flush=True)
+    heads = [0, 5, 10, 15, 17, 22, 27, 31]
+    print(f"[bwd] 1x32x4096 causal={causal} (heads {heads} sampled)", flush=True)
     dq, dk, dv = _gpu_bwd(qb, kb, vb, gb, causal, scale)
-    heads = [0, 31]
     sel = lambda x: si.bf16_bits_to_f32(x[:, heads]).astype(np.float64)
+    qf, kf, vf, gf = sel(qb), sel(kb), sel(vb), sel(gb)
     rows = np.stack([si.sample_rows(3, h, N, 1024) for h in heads])
-    rq, rk, rv = fa_oracle.attention_bwd_ref(sel(qb), sel(kb), sel(vb), sel(gb), causal, scale,
-                                             rows=rows, key_rows=rows)
-    for name, got, ref in (("dq", dq, rq), ("dk", dk, rk), ("dv", dv, rv)):
+    rq, rk, rv = fa_oracle.attention_bwd_ref(qf, kf, vf, gf, causal, scale, rows=rows, key_rows=rows)
+    bq, bk, bv = bwd_elem_bounds(qf, kf, vf, gf, causal, scale)
+    pick = lambda x: np.stack([x[:, n, rows[n]] for n in range(len(heads))], axis=1)
+    for name, got, ref, bnd in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
         got = np.stack([got[:, h, rows[n]] for n, h in enumerate(heads)], axis=1)
-        err = np.abs(got - ref)
-        rel_rms = float(np.sqrt((err ** 2).sum() / (ref ** 2).sum()))
-        scale_ref = float(np.abs(ref).max())
-        print(f"    {name}: max_abs {float(err.max()):.3e} (max |ref| {scale_ref:.3e}) rel_rms {rel_rms:.3e}",
-              flush=True)
-        assert np.isfinite(got).all()
-        # Normwise: BF16 P and dS (relative 2^-8 each, independent signs) and the
-        # rounded outputs give a relative RMS error of a few 2^-9; gate at 2^-6.
-        assert rel_rms <= 2.0 ** -6, f"{name}: relative RMS {rel_rms:.3e}"
-        assert float(err.max()) <= 2.0 ** -5 * scale_ref, f"{name}: max error {float(err.max()):.3e}"
+        check_grad(name, got, ref, pick(bnd), f"1x32x4096 causal={causal}")

@@ -28,7 +28,7 @@ def _may_split(case) -> bool:
     return fa.fwd_workspace_bytes(case.B, case.Hq, case.N, case.d) > 0
 
 
-def _run_case(case: si.FwdCase, scale=None):
+def _run_case(case: si.FwdCase, scale=None, extra_rows=()):
     import exact_tiled_attention_fa_amd as fa
     scale = case.scale if scale is None else scale
     _say(f"[fwd] {case.name} causal={case.causal} seed={case.seed} scale={scale}")
@@ -41,7 +41,12 @@ def _run_case(case: si.FwdCase, scale=None):
     del q, k, v, o, lse
     qf, kf, vf = si.bf16_bits_to_f32(qb), si.bf16_bits_to_f32(kb), si.bf16_bits_to_f32(vb)
     if case.sampled_rows:
-        rows = np.stack([si.sample_rows(case.seed, h, case.N, case.sampled_rows) for h in range(case.Hq)])
+        # Forced rows first, then the seeded sample's other rows: the same count for every head.
+        extra = np.unique(np.asarray(extra_rows, dtype=np.int64))
+        assert len(extra) < case.sampled_rows
+        rows = np.stack([np.sort(np.concatenate([
+            extra, np.setdiff1d(si.sample_rows(case.seed, h, case.N, case.sampled_rows), extra)
+                   [:case.sampled_rows - len(extra)]])) for h in range(case.Hq)])
     else:
         rows = None
     # One oracle pass over [V, |V|]: O and the P|V| term of the element bound.
@@ -80,6 +85,18 @@ def test_causal_two_blocks_per_cu(Hkv, d):
     BF16 planner runs as 8-wave blocks (heads interleaved per XCD, heaviest first); d = 64, and GQA."""
     _run_case(si.FwdCase(f"1x32x4096 d{d} causal kv{Hkv}", 1, 32, Hkv, 4096, d, True, seed=60 + d + Hkv,
                          sampled_rows=256))
+
+
+@pytest.mark.parametrize("Hq,Hkv,N,d", [(16, 16, 8000, 128), (16, 4, 8000, 64), (8, 8, 8200, 128)])
+def test_causal_eight_wave_ragged_tail(Hq, Hkv, N, d):
+    """Causal shapes the planner runs as 256-row (8-wave) blocks with N not a multiple of 256: 16 heads
+    of 8000 keys make exactly two blocks per CU, 8 heads of 8200 run unsplit. The last block is partial
+    (staged Q rows clamped, the diagonal mask and rows past N together); every row of its tail, the
+    rows at N - 256 and the first row of that block are checked beside the seeded sample."""
+    last0 = (N - 1) // 256 * 256
+    extra = sorted(set(range(last0, N)) | {N - 256, N - 255, last0 - 1})
+    _run_case(si.FwdCase(f"1x{Hq}x{N} d{d} causal kv{Hkv} (8-wave ragged)", 1, Hq, Hkv, N, d, True,
+                         seed=70 + Hq + d, sampled_rows=128), extra_rows=extra)
 
 
 @pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 24, 24, 300, 64), (2, 8, 4, 500, 128), (1, 16, 2, 190, 128)])
