@@ -18,7 +18,7 @@ import torch
 from . import _lib
 from ._lib import FaError
 
-__all__ = ["attention", "fwd", "fwd_fp8", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes",
+__all__ = ["attention", "fwd", "fwd_noalloc", "fwd_fp8", "decode", "bwd", "fwd_workspace_bytes", "decode_workspace_bytes",
            "bwd_workspace_bytes", "prepare_fwd", "prepare_fwd_fp8", "prepare_decode", "prepare_bwd",
            "FaError"]
 
@@ -61,6 +61,20 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         scale: float | None = None, out: torch.Tensor | None = None,
         lse: torch.Tensor | None = None):
     """Attention forward. q [B,Hq,N,d], k/v [B,Hkv,N,d] bf16 -> (o [B,Hq,N,d] bf16, lse [B,Hq,N] fp32)."""
+    return _fwd_call("fa_fwd", q, k, v, causal, scale, out, lse)
+
+
+def fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor, lse: torch.Tensor,
+                causal: bool = False, scale: float | None = None):
+    """fwd through fa_fwd_noalloc: the library allocates nothing (key-split
+    partials in its static per-GPU scratch), and the caller passes out and lse.
+    Calls that may overlap on one GPU must be ordered by the caller."""
+    if out is None or lse is None:
+        raise ValueError("fwd_noalloc writes into caller-provided out and lse")
+    return _fwd_call("fa_fwd_noalloc", q, k, v, causal, scale, out, lse)
+
+
+def _fwd_call(entry: str, q, k, v, causal, scale, out, lse):
     for name, t in (("q", q), ("k", k), ("v", v)):
         _check_bf16(name, t, 4)
     B, Hq, N, d = q.shape
@@ -80,9 +94,9 @@ def fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool = False,
         raise ValueError("lse must be a contiguous float32 [B,Hq,N] tensor")
     dev = _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     with torch.cuda.device(dev):
-        st = _lib.lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
-                               B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(dev))
-    _lib.check(st, "fa_fwd")
+        st = getattr(_lib.lib(), entry)(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
+                                        B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), _stream_handle(dev))
+    _lib.check(st, entry)
     return out, lse
 
 

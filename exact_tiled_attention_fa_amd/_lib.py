@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_PKG, "libfa.so")
 FA_OK = 0
 STATUS_NAMES = {
     0: "FA_OK", -1: "FA_ERR_NULL", -2: "FA_ERR_SHAPE", -3: "FA_ERR_HEAD_DIM", -4: "FA_ERR_GQA",
-    -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG",
+    -5: "FA_ERR_ALIGN", -6: "FA_ERR_WORKSPACE", -7: "FA_ERR_LAUNCH", -8: "FA_ERR_ARG", -9: "FA_ERR_SCRATCH",
 }
 
 _lib = None
@@ -60,6 +60,10 @@ def _declare(lib):
     lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_fwd_ws.restype = ctypes.c_int
+    lib.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
+    lib.fa_fwd_noalloc.restype = ctypes.c_int
+    lib.fa_fwd_noalloc_max_scratch_bytes.argtypes = []
+    lib.fa_fwd_noalloc_max_scratch_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_fp8.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_fp8.restype = ctypes.c_int
     lib.fa_fwd_fp8_ws.argtypes = [vp, vp, vp, f, f, f, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]

@@ -4,6 +4,7 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "fa.h"
 #include "fa_launch.h"
@@ -73,6 +74,9 @@ extern "C" const char* fa_status_string(int status) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or too small";
     case FA_ERR_LAUNCH: return "FA_ERR_LAUNCH: a HIP launch failed";
     case FA_ERR_ARG: return "FA_ERR_ARG: causal must be 0 or 1 and the scales finite";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the key-split partials of these sizes exceed fa_fwd_noalloc's static scratch "
+             "(fa_fwd_noalloc_max_scratch_bytes())";
     default: return "unknown fa_status";
   }
 }
@@ -211,6 +215,58 @@ extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, floa
   st = launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws, s);
   const hipError_t ef = hipFreeAsync(ws, s);
   return (st == FA_OK && ef == hipSuccess) ? FA_OK : (st != FA_OK ? st : FA_ERR_LAUNCH);
+}
+
+// ---- fa_fwd_noalloc: the key-split partials live in a static device array.
+namespace {
+
+// Largest key-split partial buffer that plan_fwd makes on a 256-CU part is
+// 32.4 MiB (one head of 65,280 keys at d = 128, two splits of 256-row blocks);
+// the array covers it with room to spare.
+constexpr size_t kScratchBytes = (size_t)34 << 20;
+constexpr int kMaxDevices = 64;
+
+// One copy per GPU, kept until the process ends. In host code this name is a
+// host-side stand-in, not a device address: host code uses only the address
+// hipGetSymbolAddress returns for the current device (scratch_on_device).
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up on the first
+// call for that device (null if the lookup fails).
+void* scratch_on_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" size_t fa_fwd_noalloc_max_scratch_bytes(void) { return kScratchBytes; }
+
+extern "C" int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                              int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                              fa_stream_t stream) {
+  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, false);
+  if (p.ws_bytes > kScratchBytes) return FA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (p.ws_bytes > 0 && !(ws = scratch_on_device())) return FA_ERR_LAUNCH;
+  // Every non-empty split writes all of its partial rows before the combine
+  // reads them, and the combine reads no other split, so the array needs no
+  // clearing between calls.
+  return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, ws,
+                            reinterpret_cast<hipStream_t>(stream));
 }
 
 namespace {

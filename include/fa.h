@@ -35,7 +35,8 @@
  *   - scale is used exactly as given (any finite value, including 0 and
  *     negative); the usual choice is 1/sqrt(d).
  *   - The functions are thread-safe; concurrent calls on different streams do
- *     not share memory unless the caller passes the same buffers.
+ *     not share memory unless the caller passes the same buffers (except
+ *     fa_fwd_noalloc, whose calls on one GPU share its static scratch).
  */
 #ifndef FA_H_
 #define FA_H_
@@ -60,7 +61,8 @@ typedef enum {
   FA_ERR_ALIGN = -5,     /* a tensor pointer is not 16-byte aligned (lse: 4-byte) */
   FA_ERR_WORKSPACE = -6, /* workspace NULL or smaller than the queried size */
   FA_ERR_LAUNCH = -7,    /* a HIP launch or allocation failed */
-  FA_ERR_ARG = -8        /* causal not 0/1, or a scale (factor) not finite */
+  FA_ERR_ARG = -8,       /* causal not 0/1, or a scale (factor) not finite */
+  FA_ERR_SCRATCH = -9    /* fa_fwd_noalloc: the key-split partials exceed its static scratch */
 } fa_status;
 
 /*
@@ -106,6 +108,30 @@ size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d);
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
               void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): same operation, arguments, layouts and kernels, but the key-split
+ * partials go to a static device array of fa_fwd_noalloc_max_scratch_bytes()
+ * bytes (34 MiB) that the library holds on each GPU it runs on until the process
+ * ends. The call itself allocates nothing; its first call on a device only looks
+ * up that device's copy of the array (hipGetSymbolAddress).
+ *
+ * Shapes whose partials (fa_fwd_workspace_bytes-sized; 17.0 MB for one head of
+ * 8192 keys at d = 128) exceed the array return FA_ERR_SCRATCH before any
+ * launch. On a 256-CU GPU no valid shape does. Every call on one GPU shares
+ * that GPU's array: calls that may overlap on one GPU (different streams,
+ * different host threads) race and must be ordered by the caller. Each call
+ * writes every partial it reads, so the array keeps the last call's contents
+ * and needs no clearing.
+ */
+int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                   fa_stream_t stream);
+
+/* Size in bytes of fa_fwd_noalloc's static per-GPU scratch array. */
+size_t fa_fwd_noalloc_max_scratch_bytes(void);
 
 /*
  * fa_fwd_fp8 -- attention forward pass on FP8 inputs ("Why is standard

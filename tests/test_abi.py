@@ -28,6 +28,7 @@ def lib():
 def test_header_declares_the_abi():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_varlen",
                                      "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_ws",
+                                     "fa_fwd_noalloc", "fa_fwd_noalloc_max_scratch_bytes",
                                      "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_status_string"]
 
 
@@ -65,6 +66,31 @@ def fwd(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0
 ])
 def test_fwd_rejects(lib, kw, status):
     assert fwd(lib, **kw) == status
+
+
+def fwd_noalloc(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0, scale=0.125):
+    return lib.fa_fwd_noalloc(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(lse=None), -1), (dict(N=0), -2), (dict(d=80), -3), (dict(Hq=3, Hkv=2), -4),
+    (dict(k=BAD), -5), (dict(causal=2), -8), (dict(scale=float("nan")), -8), (dict(N=(1 << 30) + 1), -2),
+])
+def test_fwd_noalloc_rejects(lib, kw, status):
+    assert fwd_noalloc(lib, **kw) == status
+
+
+def test_fwd_noalloc_scratch_covers_every_plan(lib):
+    """The static scratch holds the key-split partials of every shape the planner
+    splits (on the CU count the planner sees here: 256 without a GPU)."""
+    most = lib.fa_fwd_noalloc_max_scratch_bytes()
+    assert most == 34 << 20
+    worst = 0
+    for heads in range(1, 130):
+        for N in list(range(1024, 70000, 256)) + [65280, 8192]:
+            for d in (64, 128):
+                worst = max(worst, lib.fa_fwd_workspace_bytes(1, heads, N, d))
+    assert 0 < worst <= most
 
 
 def fwd_ws(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0, scale=0.125, ws=P, wsb=0):
