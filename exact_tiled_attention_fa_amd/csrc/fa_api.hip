@@ -51,10 +51,6 @@ int device_cu_count() {
   return cus;
 }
 
-// Fewest key tiles a split may hold: shorter splits spend too much of their
-// time in the prologue and the partial-result write.
-constexpr int kMinSplitTiles = 8;
-
 int next_pow2_le16(int g) {
   int p = 1;
   while (p < g && p < 16) p <<= 1;
@@ -107,44 +103,10 @@ int check_fwd_sizes(int B, int Hq, int N, int d) {
   return FA_OK;
 }
 
-struct FwdPlan {
-  int rows, nqb, n_splits, split_tiles;
-  int head_group;    // see FwdArgs::head_group
-  int64_t nwg;       // work-groups of the forward launch
-  size_t ws_bytes;   // partial-result buffer for a split, 0 otherwise
-};
+using fa::FwdPlan;
 
-// Key split for grids that would leave CUs idle: aim at as many work-groups
-// as fit on the CUs at once (one of 8 waves or two of 4 per CU), never fewer
-// than kMinSplitTiles key tiles per split.
 FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal, bool fp8) {
-  FwdPlan p;
-  const int waves = fa::fwd_waves(causal, N, (int64_t)B * Hq * ((N + 255) / 256), device_cu_count(), fp8);
-  p.rows = fa::kFwdWaveRows * waves;
-  // Causal blocks differ in work (heaviest first). Each of the 8 XCDs takes a
-  // contiguous range of the grid; when that range is a whole number (>= 2) of
-  // heads, their blocks interleave so the XCD starts all its heaviest blocks
-  // first instead of one head's after another's lightest.
-  const int64_t nbh = (int64_t)B * Hq;
-  p.head_group = causal && nbh % 8 == 0 && nbh >= 16 ? (int)(nbh / 8) : 1;
-  p.nqb = (N + p.rows - 1) / p.rows;
-  const int64_t base = (int64_t)B * Hq * p.nqb;
-  const int tiles = (N + fa::kFwdKeys - 1) / fa::kFwdKeys;
-  p.n_splits = 1;
-  p.split_tiles = tiles;
-  const int64_t target = (waves == 8 ? 1 : 2) * (int64_t)device_cu_count();
-  if (base < target && tiles >= 2 * kMinSplitTiles) {
-    const int64_t want = (target + base - 1) / base;
-    p.n_splits = (int)(want < tiles / kMinSplitTiles ? want : tiles / kMinSplitTiles);
-    p.split_tiles = (tiles + p.n_splits - 1) / p.n_splits;
-    p.n_splits = (tiles + p.split_tiles - 1) / p.split_tiles;
-  }
-  p.nwg = base * p.n_splits;
-  const size_t rows = (size_t)B * Hq * N;
-  // BF16 partial outputs, then FP32 partial lse values.
-  const size_t bytes = p.n_splits > 1 ? rows * p.n_splits * ((size_t)d * 2 + sizeof(float)) : 0;
-  p.ws_bytes = (bytes + 255) & ~(size_t)255;
-  return p;
+  return fa::plan_fwd(B, Hq, N, d, causal, fp8, device_cu_count());
 }
 
 int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -164,6 +126,8 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
   a.head_group = p.head_group;
+  a.split_target = p.split_target;
+  a.per_head = p.per_head;
   a.o_part = static_cast<uint16_t*>(ws);
   a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = 1.f;
@@ -299,6 +263,8 @@ int launch_fwd_fp8_planned(const FwdPlan& p, const void* q, const void* k, const
   a.n_splits = p.n_splits;
   a.split_tiles = p.split_tiles;
   a.head_group = p.head_group;
+  a.split_target = 0;  // the FP8 kernel takes uniform splits only
+  a.per_head = 0;
   a.o_part = static_cast<uint16_t*>(ws);
   a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = v_scale;

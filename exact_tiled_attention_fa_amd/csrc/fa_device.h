@@ -122,7 +122,7 @@ __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float
 // w_s = e^(lse_s - M), O = sum_s w_s O_s / sum_s w_s and lse = M + ln sum_s w_s.
 // op points at column col of partial 0 (partials D values apart, col a
 // multiple of 8, so each partial is one 16-byte load), lp at the row's S lse
-// values. With S <= 8 all loads go out together (the partials do not depend
+// values. With S <= 16 all loads go out together (the partials do not depend
 // on the lse values); otherwise eight partials at a time after a first pass
 // for M. O goes to o8 (eight BF16, nearest even); lse is written when
 // write_lse.
@@ -161,6 +161,29 @@ __device__ __forceinline__ void merge_splits8(const uint16_t* __restrict__ op, c
       wsum += w;
 #pragma unroll
       for (int c = 0; c < 8; ++c) acc[c] = fmaf(w, v[u][c], acc[c]);
+    }
+  } else if (S <= 16) {
+    // Every load in one round trip: partial u reads partial min(u, S - 1)
+    // (no branch per load) and the copies past S - 1 get weight 0.
+    float l[16];
+    uint4 w[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int su = u < S ? u : S - 1;
+      l[u] = lp[su];
+      w[u] = *reinterpret_cast<const uint4*>(op + (size_t)su * D);
+    }
+#pragma unroll
+    for (int u = 0; u < 16; ++u) M = fmaxf(M, l[u]);
+    const float Ms = M == -INFINITY ? 0.f : M;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const float wt = u < S ? exp2_hw((l[u] - Ms) * kLog2e) : 0.f;
+      wsum += wt;
+      const float v[8] = {bf16_lo(w[u].x), bf16_hi(w[u].x), bf16_lo(w[u].y), bf16_hi(w[u].y),
+                          bf16_lo(w[u].z), bf16_hi(w[u].z), bf16_lo(w[u].w), bf16_hi(w[u].w)};
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[c] = fmaf(wt, v[c], acc[c]);
     }
   } else {
     for (int s0 = 0; s0 < S; s0 += 8) {

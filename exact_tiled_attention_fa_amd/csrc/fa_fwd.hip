@@ -103,28 +103,23 @@ void fa_fwd_kernel(FwdArgs a) {
   // when every work-group starts at once (8 XCDs reading all of Q cost the
   // 1-head 8K call 4%), while K/V chunks are streamed once per XCD.
   const int lid = xcd_contiguous(blockIdx.x, a.nwg);
-  const int per_head = a.nqb * a.n_splits;
-  const int grp = lid / (a.head_group * per_head);
-  const int rem_g = lid - grp * a.head_group * per_head;
-  const int gh = min(a.head_group, a.B * a.Hq - grp * a.head_group);  // heads in this group
-  const int qs = rem_g / gh;
-  const int bh = grp * a.head_group + (rem_g - qs * gh);
-  int qb = qs / a.n_splits;
-  const int split = qs - qb * a.n_splits;
-  if (CAUSAL) qb = a.nqb - 1 - qb;
+  int qb, split, bh;
+  int split_tiles;   // key tiles per split of this block
+  int block_splits;  // splits of this block (1: it writes O and lse itself)
+  fwd_block_map(lid, a, CAUSAL, qb, split, bh, split_tiles, block_splits);
   const int b = bh / a.Hq;
   const int h = bh - b * a.Hq;
   const int hk = h / (a.Hq / a.Hkv);
   const int N = a.N;
   const int q0 = qb * C::ROWS;
   const size_t qo_base = (size_t)(b * a.Hq + h) * (size_t)N * D;
-  const int t_begin = split * a.split_tiles;
+  const int t_begin = split * split_tiles;
   const uint16_t* kg = a.k + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
   const uint16_t* vg = a.v + ((size_t)(b * a.Hkv + hk) * (size_t)N + (size_t)t_begin * kFwdKeys) * D;
   const int n_keys = N - t_begin * kFwdKeys;  // keys from the split's first one to the end
 
   const int kv_end = CAUSAL ? min(N, q0 + C::ROWS) : N;
-  const int n_tiles = min((kv_end + kFwdKeys - 1) / kFwdKeys, t_begin + a.split_tiles) - t_begin;
+  const int n_tiles = min((kv_end + kFwdKeys - 1) / kFwdKeys, t_begin + split_tiles) - t_begin;
   if (n_tiles <= 0) return;  // this split lies past the block's last visible key
 
   // Every wave takes every tile of its block; with causal masking the last
@@ -471,7 +466,7 @@ void fa_fwd_kernel(FwdArgs a) {
   const float lse_v = l_tot > 0.f ? (m_run + log2_hw(l_tot)) * kLn2 : -INFINITY;
   const size_t head_row0 = (size_t)(b * a.Hq + h) * N;
   if (qi < N && g == 0) {
-    if (a.n_splits == 1) a.lse[head_row0 + qi] = lse_v;
+    if (block_splits == 1) a.lse[head_row0 + qi] = lse_v;
     else a.lse_part[(head_row0 + qi) * a.n_splits + split] = lse_v;
   }
   __syncthreads();  // every wave is done with the K/V buffers
@@ -493,8 +488,8 @@ void fa_fwd_kernel(FwdArgs a) {
   constexpr int CPR16 = D / 8;
   constexpr int RPI = 64 / CPR16;
   const int c16 = lane % CPR16;
-  uint16_t* const dst = a.n_splits == 1 ? a.o + qo_base : a.o_part + (head_row0 * a.n_splits + split) * D;
-  const size_t row_stride = (size_t)a.n_splits * D;
+  uint16_t* const dst = block_splits == 1 ? a.o + qo_base : a.o_part + (head_row0 * a.n_splits + split) * D;
+  const size_t row_stride = block_splits == 1 ? (size_t)D : (size_t)a.n_splits * D;
 #pragma unroll
   for (int i = 0; i < 32 / RPI; ++i) {
     const int r = RPI * i + lane / CPR16;
@@ -531,7 +526,13 @@ __global__ __launch_bounds__(kMergeThreads) void fa_fwd_combine_kernel(FwdArgs a
   const int col = 8 * (threadIdx.x % LPR);
   const int kv_end = CAUSAL ? min(a.N, qb * a.rows + a.rows) : a.N;
   const int tiles = (kv_end + kFwdKeys - 1) / kFwdKeys;
-  const int S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
+  int S;
+  if (CAUSAL && a.split_target > 0) {
+    S = (tiles + a.split_target - 1) / a.split_target;
+    if (S == 1) return;  // the block's only split wrote O and lse itself
+  } else {
+    S = min(a.n_splits, (tiles + a.split_tiles - 1) / a.split_tiles);
+  }
   merge_splits8<D>(a.o_part + row * a.n_splits * D + col, a.lse_part + row * a.n_splits, S, a.o + row * D + col,
                    a.lse + row, col == 0);
 }

@@ -186,6 +186,18 @@ def test_equal_keys_give_mean_of_values_at_full_size():
     check_lse(to_f64(lse)[0, 0], s + np.log(np.arange(1, N + 1)), "equal keys causal lse")
 
 
+@pytest.mark.parametrize("B,Hq,Hkv,N,d", [(1, 1, 1, 8192, 64), (1, 1, 1, 16384, 128), (2, 1, 1, 12000, 128),
+                                         (1, 2, 1, 4096, 128), (1, 3, 3, 3000, 64), (1, 8, 2, 2048, 128),
+                                         (1, 1, 1, 8200, 128), (1, 2, 2, 9001, 64)])
+def test_causal_split_per_block(B, Hq, Hkv, N, d):
+    """Causal grids too small for the CUs split each block's keys by its own visible tiles (the heavy
+    blocks into more splits, blocks that fit one split written directly); ragged N, GQA and d = 64 too."""
+    rows = 256 if N > 4096 else None
+    extra = [N - 1, N - 2, N - 64, N - 65] if rows else ()
+    _run_case(si.FwdCase(f"causal split B{B} Hq{Hq} Hkv{Hkv} N{N} d{d}", B, Hq, Hkv, N, d, True,
+                         seed=1700 + N + d + Hq, sampled_rows=rows), extra_rows=extra)
+
+
 @pytest.mark.parametrize("B,H,N,d,causal", [(1, 1, 4096, 128, False), (1, 2, 3000, 64, True),
                                             (1, 1, 1100, 128, True), (2, 1, 2500, 128, False)])
 def test_key_split_path(B, H, N, d, causal):
