@@ -52,6 +52,17 @@ METRIC = "attention fwd TFLOP/s & % BF16 MFMA peak (N=8K,d=128); decode HBM GB/s
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense BF16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
+# The analytic H100 figures of "FlashAttention HBM bytes, one head, 8K" ("A strong
+# answer"): a model of one 8K head at d = 128 on an H100 SXM, printed there for context.
+# They are the page's model, not measurements and not this build's target.
+PAGES_H100_MODEL = {
+    "source": "FlashAttention HBM bytes, one head, 8K (A strong answer): analytic model, not measured",
+    "h100_bf16_dense_tflops": 989.0,
+    "h100_hbm_tbs": 3.35,
+    "fwd_1x1x8192_d128_compute_floor_us": 34.7,
+    "fwd_1x1x8192_d128_naive_us": 163.0,
+    "fwd_1x1x8192_d128_hbm_floor_us": 2.5,
+}
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "fa_fwd_1x1x8192_d128_counters.txt")
 KERNEL_SOURCES = ["fa_fwd.hip", "fa_device.h", "fa_launch.h"]
 
@@ -213,8 +224,9 @@ def run_only(name: str, reps: int) -> None:
                       "unit": unit}), flush=True)
 
 
-def cpu_baseline(case, seconds: float) -> dict:
-    """The FP64 oracle as it stands, timed on this host's cores over whole passes of the workload."""
+def cpu_baseline(case, seconds: float, gpu_outputs=None) -> dict:
+    """The FP64 oracle as it stands, timed on this host's cores over whole passes of the workload;
+    with gpu_outputs, also the GPU results' errors against it per workload config."""
     import numpy as np
     import seeded_inputs as si
     from oracle import fa_oracle
@@ -239,7 +251,38 @@ def cpu_baseline(case, seconds: float) -> dict:
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
             "sample": f"{passes} full pass(es) of the 1x1x8192 d128 non-causal forward ({rows_total} rows) "
                       f"in {dt:.1f} s, FP64 NumPy three-pass attention",
-            "seconds_by_config": oracle_seconds_by_config()}
+            "seconds_by_config": oracle_seconds_by_config(),
+            "parity_by_config": parity_by_config(gpu_outputs) if gpu_outputs else None}
+
+
+def parity_by_config(gpu_outputs: dict) -> dict:
+    """Errors of this run's GPU results against the FP64 oracle, per workload config, on the rows
+    the parity tests check (every row of the tiny, 8K and decode configs; the seeded 1,024 rows
+    per head of the 32-head 4K and 128K ones). gpu_outputs[name] = (case, o, lse, rows) with o and
+    lse numpy arrays of exactly those rows (rows None = all). Tolerances: O max abs <= 1e-2 and
+    |dlse| / max(|lse|, 1) <= 1e-3."""
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import fa_oracle
+    out = {}
+    for name, (case, o_gpu, lse_gpu, rows, inputs) in gpu_outputs.items():
+        t0 = time.perf_counter()
+        q, k, v = (si.bf16_bits_to_f32(x) for x in inputs)
+        if isinstance(case, si.DecodeCase):
+            o_ref, lse_ref = fa_oracle.decode_ref(q, k, v, case.scale)
+        else:
+            o_ref, lse_ref = fa_oracle.attention_ref(q, k, v, case.causal, case.scale, rows=rows)
+        err = np.abs(o_gpu.astype(np.float64) - o_ref)
+        lrel = np.abs(lse_gpu.astype(np.float64) - lse_ref) / np.maximum(np.abs(lse_ref), 1.0)
+        o_max, l_max = float(err.max()), float(lrel.max())
+        out[name] = {"rows_checked": int(o_ref.shape[-2] * o_ref.shape[1] * o_ref.shape[0])
+                     if not isinstance(case, si.DecodeCase) else int(o_ref.shape[0] * o_ref.shape[1]),
+                     "o_max_abs": float(f"{o_max:.3e}"),
+                     "o_rel_rms": float(f"{float(np.sqrt((err ** 2).sum() / (o_ref ** 2).sum())):.3e}"),
+                     "lse_max_rel": float(f"{l_max:.3e}"),
+                     "pass": bool(o_max <= 1e-2 and l_max <= 1e-3),
+                     "oracle_s": round(time.perf_counter() - t0, 2)}
+    return out
 
 
 def oracle_seconds_by_config(cases=None, decode_cases=None) -> dict:
@@ -386,7 +429,56 @@ def main() -> int:
     dec_gbs = kv_bytes / t_dec / 1e9
 
     extra = {}
+    gpu_outputs = {}  # per workload config: GPU results on the rows the oracle checks
+
+    def sampled(case, o_t, l_t):
+        rows = (np.stack([si.sample_rows(case.seed, h, case.N, case.sampled_rows) for h in range(case.Hq)])
+                if case.sampled_rows else None)
+        o_np = o_t.float().cpu().numpy()
+        l_np = l_t.float().cpu().numpy()
+        if rows is not None:
+            o_np = np.stack([o_np[:, h, rows[h]] for h in range(case.Hq)], axis=1)
+            l_np = np.stack([l_np[:, h, rows[h]] for h in range(case.Hq)], axis=1)
+        return o_np, l_np, rows
+
+    if not args.no_cpu_baseline:
+        torch.cuda.synchronize()
+        fin = si.fwd_inputs(fcase)
+        gpu_outputs[fcase.name] = (fcase, *sampled(fcase, o, lse)[:2], None, fin)
+        gpu_outputs[si.ONE_HEAD_8K_CAUSAL.name] = (si.ONE_HEAD_8K_CAUSAL, *sampled(si.ONE_HEAD_8K_CAUSAL, o_c,
+                                                                                    lse_c)[:2], None, fin)
+        gpu_outputs[dcase.name] = (dcase, do.float().cpu().numpy()[:, :, 0], dlse.float().cpu().numpy(), None,
+                                   si.decode_inputs(dcase))
+        tin = si.fwd_inputs(si.TINY)
+        qt, kt, vt = (up(x) for x in tin)
+        ot, lt = fa.fwd(qt, kt, vt, causal=False, scale=si.TINY.scale)
+        torch.cuda.synchronize()
+        gpu_outputs[si.TINY.name] = (si.TINY, *sampled(si.TINY, ot, lt)[:2], None, tin)
+        del qt, kt, vt, ot, lt
+
     if not args.no_extra:
+        # The named fa_fwd entry point at the headline shape: on its key-split path it takes a
+        # stream-ordered temporary buffer per call (hipMallocAsync / hipFreeAsync) where fa_fwd_ws,
+        # timed above, uses a caller workspace.
+        lib = fa._lib.lib()
+        st_h = stream.cuda_stream
+        o_x = torch.empty_like(q)
+        l_x = torch.empty_like(lse)
+
+        def run_fa_fwd():
+            fa._lib.check(lib.fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_x.data_ptr(), l_x.data_ptr(),
+                                     1, 1, 1, fcase.N, fcase.d, 0, fcase.scale, st_h), "fa_fwd")
+
+        def run_noalloc():
+            fa._lib.check(lib.fa_fwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_x.data_ptr(),
+                                             l_x.data_ptr(), 1, 1, 1, fcase.N, fcase.d, 0, fcase.scale, st_h),
+                          "fa_fwd_noalloc")
+        for key, fn in (("fwd_1x1x8192_d128_fa_fwd", run_fa_fwd), ("fwd_1x1x8192_d128_fa_fwd_noalloc", run_noalloc)):
+            settle(fn, 0.2)
+            t = per_call_s(fn, reps)
+            extra[key] = {"us": round(t * 1e6, 2), "tflops": round(flops / t / 1e12, 2),
+                          "frac_peak": round(flops / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del o_x, l_x
         # Cold caches: before each of 50 single calls a 1 GiB buffer is read
         # (more than the 256 MiB last-level cache; reading leaves clean lines,
         # where a write would leave write-backs to compete with the call), then
@@ -414,25 +506,24 @@ def main() -> int:
                 extra[key] = {"us_median": round(med * 1e6, 2), "us_min": round(best * 1e6, 2),
                               "tflops_median": round(fl / med / 1e12, 2)}
         del flush
-        for case in (si.HEADS32_4K, si.HEADS32_4K_CAUSAL):
-            q3, k3, v3 = (up(x) for x in si.fwd_inputs(case))
+        # The 32-head 4K forward both ways and the long-context 128K causal forward (each
+        # call ~28 ms, so 3 timed calls).
+        for case, nrep in ((si.HEADS32_4K, 10), (si.HEADS32_4K_CAUSAL, 10), (si.LONG_128K, 3)):
+            fin3 = si.fwd_inputs(case)
+            q3, k3, v3 = (up(x) for x in fin3)
             o3 = torch.empty_like(q3)
             l3 = torch.empty((case.B, case.Hq, case.N), dtype=torch.float32, device=dev)
             run3 = fa.prepare_fwd(q3, k3, v3, o3, l3, causal=case.causal, scale=case.scale)
             settle(run3, 0.2)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 10
-            a.record(stream)
-            for _ in range(reps):
-                run3()
-            b.record(stream)
-            torch.cuda.synchronize()
-            t = a.elapsed_time(b) * 1e-3 / reps
+            t = per_call_s(run3, nrep)
             fl = 4.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
-            key = "fwd_1x32x4096_d128" + ("_causal" if case.causal else "")
+            key = f"fwd_{case.B}x{case.Hq}x{case.N}_d{case.d}" + ("_causal" if case.causal else "")
             extra[key] = {"us": round(t * 1e6, 2), "tflops": round(fl / t / 1e12, 2),
                           "frac_peak": round(fl / t / 1e12 / PEAK_BF16_TFLOPS, 4)}
-            del q3, k3, v3, o3, l3
+            if not args.no_cpu_baseline:
+                torch.cuda.synchronize()
+                gpu_outputs[case.name] = (case, *sampled(case, o3, l3), fin3)
+            del q3, k3, v3, o3, l3, fin3
         # FP8 forward at the 32-head 4K shape (E4M3 inputs quantised per tensor from
         # the same seeded draws); the peak it is quoted against is the FP8 one.
         for case in (si.HEADS32_4K, si.HEADS32_4K_CAUSAL):
@@ -505,9 +596,10 @@ def main() -> int:
         "decode_us": round(t_dec * 1e6, 2),
         "also": extra,
         "rocprof_counters": measured_counters(),
+        "pages_h100_model": PAGES_H100_MODEL,
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(fcase, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(fcase, args.cpu_seconds, gpu_outputs)
     print(json.dumps(result), flush=True)
     return 0
 

@@ -78,3 +78,27 @@ def test_oracle_seconds_by_config_scales_one_head():
     d = r["tiny decode"]
     assert d["sequences"] == 2 and d["rows"] == 8
     assert d["seconds"] == pytest.approx(2 * d["seconds_one_sequence"], abs=2e-3)
+
+
+def test_parity_by_config_reports_errors_against_the_oracle():
+    """The bench's per-config parity report: stand-in results (the oracle's own values, then
+    the same moved by a known amount) give the expected errors and pass flags."""
+    import dataclasses
+    import numpy as np
+    import seeded_inputs as si
+    from oracle import fa_oracle
+    case = dataclasses.replace(si.TINY, name="tiny sampled", Hq=2, Hkv=2, N=200, sampled_rows=40)
+    inputs = si.fwd_inputs(case)
+    rows = np.stack([si.sample_rows(case.seed, h, case.N, case.sampled_rows) for h in range(case.Hq)])
+    q, k, v = (si.bf16_bits_to_f32(x) for x in inputs)
+    o_ref, lse_ref = fa_oracle.attention_ref(q, k, v, case.causal, case.scale, rows=rows)
+    dec = si.DecodeCase("tiny decode", 2, 4, 2, 64, 64, 4, seed=1)
+    dinp = si.decode_inputs(dec)
+    od, ld = fa_oracle.decode_ref(*(si.bf16_bits_to_f32(x) for x in dinp), dec.scale)
+    good = bench.parity_by_config({"a": (case, o_ref, lse_ref, rows, inputs), "d": (dec, od, ld, None, dinp)})
+    assert good["a"]["pass"] and good["a"]["o_max_abs"] < 1e-12 and good["a"]["rows_checked"] == 80
+    assert good["d"]["pass"] and good["d"]["rows_checked"] == 8
+    bad = bench.parity_by_config({"a": (case, o_ref + 0.02, lse_ref * (1 + 2e-3) + 2e-3, rows, inputs)})
+    assert not bad["a"]["pass"]
+    assert bad["a"]["o_max_abs"] == pytest.approx(0.02, rel=1e-6)
+    assert bad["a"]["lse_max_rel"] >= 2e-3
