@@ -58,22 +58,47 @@ constexpr int kFwdWaveRows = 32;  // query rows per wave
 __host__ __device__ inline void fwd_block_map(int lid, const FwdArgs& a, bool causal, int& qb, int& split,
                                               int& bh, int& split_tiles, int& block_splits) {
   if (causal && a.split_target > 0) {
-    // Splits sized per block: walk the blocks heaviest first, each taking
-    // (its splits) x (heads in the group) consecutive ids. Uniform across a
-    // work-group (scalar), and short for the heavy blocks, which start first.
+    // Splits sized per block, blocks heaviest first, each taking (its splits)
+    // x (heads in the group) consecutive ids. The last block sees every key
+    // tile; a full block qb < nqb - 1 sees u R tiles (u = qb + 1, R = rows /
+    // 64) and takes ceil(u R / T) splits, which equals k exactly for u in
+    // [floor((k - 1) T / R) + 1, floor(k T / R)]. So the walk goes over the
+    // split counts k (at most the largest count, about 16) instead of over the
+    // blocks, with no division inside: every wave of the work-group runs it on
+    // the CU's one scalar unit, and a walk over 64 blocks had held the last
+    // work-groups of a 16K head up by 8 us.
+    const int T = a.split_target;
+    const int R = a.rows / kFwdKeys;  // 2 or 4: a shift below
+    const int rs = 31 - __builtin_clz((unsigned)R);
     const int per_group = a.head_group * a.per_head;
     const int grp = lid / per_group;
     int r = lid - grp * per_group;
     const int left = a.B * a.Hq - grp * a.head_group;
     const int gh = a.head_group < left ? a.head_group : left;
-    int i = 0, vis = 0, ns = 1;
-    for (;; ++i) {
-      vis = causal_block_tiles(a.nqb - 1 - i, a.rows, a.N, kFwdKeys);
-      ns = (vis + a.split_target - 1) / a.split_target;
-      if (r < ns * gh || i + 1 >= a.nqb) break;
+    int vis = causal_block_tiles(a.nqb - 1, a.rows, a.N, kFwdKeys);
+    int ns = (vis + T - 1) / T;
+    qb = a.nqb - 1;
+    if (r >= ns * gh && a.nqb > 1) {
       r -= ns * gh;
+      const int u_top = a.nqb - 1;  // full blocks: u = 1 .. u_top
+      int k = (u_top * R + T - 1) / T;
+      int u_hi = u_top;
+      for (; k > 1; --k) {
+        const int u_lo = (((k - 1) * T) >> rs) + 1;  // first u with ceil(u R / T) = k
+        const int span = (u_hi - u_lo + 1) * k * gh;
+        if (u_lo <= u_hi) {
+          if (r < span) break;
+          r -= span;
+          u_hi = u_lo - 1;
+        }
+      }
+      // Here the block is in the run of split count k ending at u_hi.
+      const int p = r / (k * gh);
+      r -= p * k * gh;
+      qb = u_hi - p - 1;
+      ns = k;
+      vis = (qb + 1) * R;
     }
-    qb = a.nqb - 1 - i;
     split = r / gh;
     bh = grp * a.head_group + (r - split * gh);
     block_splits = ns;
