@@ -27,7 +27,7 @@
 //     dS^T packed to BF16 as the B operand of dQ^T += K^T dS^T with K^T
 //     gathered by transposed reads.
 // Tiles that hold both row reads and transposed reads use a swizzle that keeps
-// both patterns free of bank conflicts (sw2 below).
+// both patterns free of bank conflicts (sw2, swq below).
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -66,6 +66,36 @@ __device__ __forceinline__ int sw2(int r) {
 template <int D>
 __device__ __forceinline__ int swr(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
+// Swizzle of the dK/dV pass's Q and dO tiles, read by rows (16 rows at one
+// chunk) and transposed with rows 4 b + (lane / 4) % 4 for 16-lane block b.
+// Two 16-lane blocks share an LDS cycle of those 8-byte reads: measured, sw2
+// (conflict-free within one block) still cost 134 M bank-conflict cycles, a
+// third of the pass, and a swizzle built for blocks (0, 1) and (2, 3) sharing
+// a cycle 67 M. This one gives distinct chunk pairs to the 8 rows of blocks
+// (0, 1), (2, 3), (0, 2) and (1, 3) alike, and distinct chunks to 16 rows:
+//   d = 128 (16 chunks per row): bits 1-2 = r & 3, bit 3 = bit 2 ^ bit 3 of r,
+//     bit 0 = bit 3 of r;
+//   d = 64 (8 chunks, two rows per bank line, parity separating them): the same
+//     construction on t = (r >> 1) & 7 in 3 bits.
+// (Checked on the CPU against a 64-bank model under both pairings.)
+template <int D>
+__device__ __forceinline__ int swq(int r) {
+  if (D == 128) {
+    const int f = (r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2);
+    return (f << 1) | ((r >> 3) & 1);
+  }
+  const int t = (r >> 1) & 7;
+  const int h = (t & 1) | ((((t >> 1) ^ (t >> 2)) & 1) << 1);
+  return (h << 1) | ((t >> 2) & 1);
+}
+
+// Swizzle kinds of a tile: rows only, sw2 (dQ's K tiles), swq (dK/dV's Q, dO).
+enum { kSwRows = 0, kSw2 = 1, kSwQ = 2 };
+template <int D, int SW>
+__device__ __forceinline__ int swz(int r) {
+  return SW == kSwQ ? swq<D>(r) : (SW == kSw2 ? sw2<D>(r) : swr<D>(r));
+}
+
 // Direct loads of the 64-row tile starting at row row0 of a row-major
 // [rows, D] BF16 matrix into LDS: wave w fills the 1 KiB blocks
 // BPW w .. BPW w + BPW - 1; lane l writes physical chunk l % CPR of its row
@@ -73,7 +103,7 @@ __device__ __forceinline__ int swr(int r) { return D == 128 ? (r & 15) : ((r >> 
 // 64-bit arithmetic, so each lane's 32-bit byte offset spans one tile (at most
 // 16 KiB) whatever the sequence length. Rows past `rows` read the last row
 // (finite data the caller masks).
-template <int D, bool SW2>
+template <int D, int SW>
 __device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int rows, uint4* dst, int wave, int lane) {
   using C = BwdCfg<D>;
   const int pc = lane % C::CPR;
@@ -83,11 +113,76 @@ __device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int row
 #pragma unroll
   for (int x = 0; x < C::BPW; ++x) {
     const int r = C::RPB * (C::BPW * wave + x) + lane / C::CPR;
-    const int sw = SW2 ? sw2<D>(r) : swr<D>(r);
+    const int sw = swz<D, SW>(r);
     const int row = min(r, last);
     dma16(base, 2u * (uint32_t)(row * D + 8 * (pc ^ sw)), l0 + 1024u * x);
   }
 }
+
+// Per-lane byte offsets, within a full 64-row tile, of load_tile's direct
+// loads. Computed once per work-group and kept in registers for the sweep: a
+// load's offset register must not be overwritten while the load is in flight,
+// so offsets computed afresh for every tile made the compiler wait for the
+// next tile's loads before the current tile's first LDS reads (which reused
+// those registers), undoing the double buffering.
+// The only ragged tile of a sweep is the last one, whose rows past the end
+// read row (rows - 1) % 64 of the tile (finite data the caller masks); its
+// clamped offsets are precomputed the same way.
+template <int D, int SW>
+struct TileOffsets {
+  uint32_t full[BwdCfg<D>::BPW];
+  uint32_t tail[BwdCfg<D>::BPW];
+  __device__ __forceinline__ TileOffsets(int wave, int lane, int rows) {
+    using C = BwdCfg<D>;
+    const int pc = lane % C::CPR;
+    const int last = (rows - 1) % kBwdTile;
+#pragma unroll
+    for (int x = 0; x < C::BPW; ++x) {
+      const int r = C::RPB * (C::BPW * wave + x) + lane / C::CPR;
+      const int sw = swz<D, SW>(r);
+      full[x] = 2u * (uint32_t)(r * D + 8 * (pc ^ sw));
+      tail[x] = 2u * (uint32_t)(min(r, last) * D + 8 * (pc ^ sw));
+    }
+  }
+};
+
+// load_tile with the precomputed offsets (row0 a multiple of 64 below `rows`).
+template <int D, int SW>
+__device__ __forceinline__ void load_tile_at(const uint16_t* src, int row0, int rows, const TileOffsets<D, SW>& t,
+                                             uint4* dst, int wave) {
+  using C = BwdCfg<D>;
+  const uint16_t* base = src + (size_t)row0 * D;
+  const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(C::BPW * wave);
+  // Two branches, each passing its precomputed registers as they are: a
+  // select would put the offsets in fresh registers again. The ragged branch
+  // issues the same instruction through a differently worded asm statement, so
+  // the compiler cannot merge the branches into one load fed by a select.
+  if (row0 + kBwdTile <= rows) {
+#pragma unroll
+    for (int x = 0; x < C::BPW; ++x) dma16(base, t.full[x], l0 + 1024u * x);
+  } else {
+#pragma unroll
+    for (int x = 0; x < C::BPW; ++x) {
+      uint32_t saved;
+      asm volatile(
+          "s_mov_b32 %0, m0\n\t"
+          "s_mov_b32 m0, %1\n\t"
+          "global_load_lds_dwordx4 %2, %3 ; ragged tile\n\t"
+          "s_mov_b32 m0, %0"
+          : "=&s"(saved)
+          : "s"(l0 + 1024u * x), "v"(t.tail[x]), "s"(base)
+          : "memory");
+    }
+  }
+}
+
+// s_waitcnt vmcnt(0) through the builtin (expcnt and lgkmcnt left at their
+// maxima, 0x0F70 in the gfx9 encoding): unlike the same instruction in inline
+// assembly, the compiler's wait-count pass sees it, so it knows that the loads
+// issued before the loop (K^T, V^T, Q^T, dO^T held in registers) are complete
+// inside the loop. With the inline-asm wait it did not, and made each tile's
+// first products wait, load by load, for the next tile's direct loads.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace
 
@@ -173,23 +268,25 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   const int per_head = n_u - u_begin;
   const int n_t = G * per_head;
 
+  const TileOffsets<D, kSwQ> toff(wave, lane, N);
+  const uint32_t st_off = 16u * (uint32_t)lane;
   auto issue = [&](int t, int buf) {
     const int hq = hk * G + t / per_head;
     const int u = u_begin + t % per_head;
     const size_t rb = (size_t)(b * a.Hq + hq);
-    load_tile<D, true>(a.q + rb * N * D, u * kBwdTile, N, q_lds[buf], wave, lane);
-    load_tile<D, true>(a.dout + rb * N * D, u * kBwdTile, N, do_lds[buf], wave, lane);
+    load_tile_at<D, kSwQ>(a.q + rb * N * D, u * kBwdTile, N, toff, q_lds[buf], wave);
+    load_tile_at<D, kSwQ>(a.dout + rb * N * D, u * kBwdTile, N, toff, do_lds[buf], wave);
     if (wave == 0 && lane < 16) {  // lse2 and delta of the tile's 64 rows (256 B each)
       const size_t off = rb * a.Npad + (size_t)u * kBwdTile;
-      dma16(a.lse2 + off, 16u * (uint32_t)lane, lds_addr(&st_lds[buf][0][0]));
-      dma16(a.delta + off, 16u * (uint32_t)lane, lds_addr(&st_lds[buf][1][0]));
+      dma16(a.lse2 + off, st_off, lds_addr(&st_lds[buf][0][0]));
+      dma16(a.delta + off, st_off, lds_addr(&st_lds[buf][1][0]));
     }
   };
 
   // Per-lane LDS byte offsets. A fragments (rows): row 16 qt + j16, chunk 4 kk + b16.
   int aoff[C::KK16];
 #pragma unroll
-  for (int kk = 0; kk < C::KK16; ++kk) aoff[kk] = 16 * (j16 * C::CPR + ((4 * kk + b16) ^ sw2<D>(j16)));
+  for (int kk = 0; kk < C::KK16; ++kk) aoff[kk] = 16 * (j16 * C::CPR + ((4 * kk + b16) ^ swq<D>(j16)));
   // Transposed reads: lane names row 4 b16 + j16 / 4 (+ 32 u2, + 16 for the
   // second half) and 4 columns at 16 tt + 4 (j16 % 4); lane l receives column
   // 16 tt + j16 of rows 4 b16 .. 4 b16 + 3.
@@ -198,7 +295,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     const int r0 = 4 * b16 + (j16 >> 2);
 #pragma unroll
     for (int tt = 0; tt < C::TT; ++tt)
-      troff[tt] = 16 * (r0 * C::CPR + ((2 * tt + ((j16 & 3) >> 1)) ^ sw2<D>(r0))) + 8 * (j16 & 1);
+      troff[tt] = 16 * (r0 * C::CPR + ((2 * tt + ((j16 & 3) >> 1)) ^ swq<D>(r0))) + 8 * (j16 & 1);
   }
 
   f32x4 dk[C::TT], dv[C::TT];
@@ -209,7 +306,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   issue(0, 0);  // n_t >= 1: the key block lies below N
   for (int t = 0; t < n_t; ++t) {
     const int buf = t & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem_all();
     __syncthreads();
     if (t + 1 < n_t) issue(t + 1, buf ^ 1);
     const int u = u_begin + t % per_head;
@@ -318,8 +415,10 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const int kv_end = CAUSAL ? min(N, q0 + kBwdRowBlock) : N;
   const int n_tiles = (kv_end + kBwdTile - 1) / kBwdTile;
 
-  load_tile<D, true>(kg, 0, N, k_lds[0], wave, lane);
-  load_tile<D, false>(vg, 0, N, v_lds[0], wave, lane);
+  const TileOffsets<D, kSw2> koffs(wave, lane, N);
+  const TileOffsets<D, kSwRows> voffs(wave, lane, N);
+  load_tile_at<D, kSw2>(kg, 0, N, koffs, k_lds[0], wave);
+  load_tile_at<D, kSwRows>(vg, 0, N, voffs, v_lds[0], wave);
 
   // Q^T and dO^T as B operands (lane = query row qi), lse2 and delta of qi.
   bf16x8 qf[C::KK32], df[C::KK32];
@@ -365,11 +464,11 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
 
   for (int t = 0; t < n_tiles; ++t) {
     const int buf = t & 1;
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    wait_vmem_all();
     __syncthreads();
     if (t + 1 < n_tiles) {
-      load_tile<D, true>(kg, (t + 1) * kBwdTile, N, k_lds[buf ^ 1], wave, lane);
-      load_tile<D, false>(vg, (t + 1) * kBwdTile, N, v_lds[buf ^ 1], wave, lane);
+      load_tile_at<D, kSw2>(kg, (t + 1) * kBwdTile, N, koffs, k_lds[buf ^ 1], wave);
+      load_tile_at<D, kSwRows>(vg, (t + 1) * kBwdTile, N, voffs, v_lds[buf ^ 1], wave);
     }
     const int kv0 = t * kBwdTile;
     const char* kb = reinterpret_cast<const char*>(k_lds[buf]);
