@@ -304,33 +304,47 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
 
   const float c = a.c;
   issue(0, 0);  // n_t >= 1: the key block lies below N
-  for (int t = 0; t < n_t; ++t) {
-    const int buf = t & 1;
-    wait_vmem_all();
-    __syncthreads();
-    if (t + 1 < n_t) issue(t + 1, buf ^ 1);
-    const int u = u_begin + t % per_head;
-    const int i0 = u * kBwdTile;
+  // One query tile; the buffer index is a compile-time constant (the loop
+  // takes two tiles per trip), so every LDS address is a register plus an
+  // immediate: with a run-time index each of the tile's 96 reads took an
+  // address add.
+  // The products and weights of one query tile, MASKED for the tiles that hold
+  // keys past N, rows past N or (causal) keys above a row: the last key
+  // block, the last query tile and the diagonal tile. The others take no mask
+  // (a mask in every tile turned into a branch per weight).
+  auto tile_body = [&](auto buf_c, auto mask_c, int i0) {
+    constexpr int buf = decltype(buf_c)::value;
+    constexpr bool MASKED = decltype(mask_c)::value != 0;
     const char* qb = reinterpret_cast<const char*>(q_lds[buf]);
     const char* db = reinterpret_cast<const char*>(do_lds[buf]);
 
-    // S = Q K^T and dP = dO V^T for 4 groups of 16 query rows.
+    // S = Q K^T and dP = dO V^T for the group of 16 query rows qt, from
+    // fragments read one group ahead into alternating register sets (the
+    // empty asm statements keep each set's reads where they are written: left
+    // to itself the compiler read every fragment right before its product and
+    // waited for it, one read in flight).
     f32x4 s[4], dp[4];
+    bf16x8 fq[2][C::KK16], fd[2][C::KK16];
+    auto read_a = [&](int qt) {
 #pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
+      for (int kk = 0; kk < C::KK16; ++kk) {
+        fq[qt & 1][kk] = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * C::CPR * 16);
+        fd[qt & 1][kk] = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * C::CPR * 16);
+      }
+#pragma unroll
+      for (int kk = 0; kk < C::KK16; ++kk) asm volatile("" : "+v"(fq[qt & 1][kk]), "+v"(fd[qt & 1][kk]));
+    };
+    auto sdp = [&](int qt) {
       s[qt] = f32x4{};
       dp[qt] = f32x4{};
 #pragma unroll
       for (int kk = 0; kk < C::KK16; ++kk) {
-        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * C::CPR * 16);
-        const bf16x8 da = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * C::CPR * 16);
-        s[qt] = mfma16(qa, kf[kk], s[qt]);
-        dp[qt] = mfma16(da, vf[kk], dp[qt]);
+        s[qt] = mfma16(fq[qt & 1][kk], kf[kk], s[qt]);
+        dp[qt] = mfma16(fd[qt & 1][kk], vf[kk], dp[qt]);
       }
-    }
-    // P and dS: lane holds key `key`, query rows i0 + 16 qt + 4 b16 + r.
-#pragma unroll
-    for (int qt = 0; qt < 4; ++qt) {
+    };
+    // P and dS of group qt: lane holds key `key`, query rows i0 + 16 qt + 4 b16 + r.
+    auto pds = [&](int qt) {
       const float4 l4 = st_lds[buf][0][4 * qt + b16];
       const float4 d4 = st_lds[buf][1][4 * qt + b16];
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
@@ -339,31 +353,72 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
       for (int r = 0; r < 4; ++r) {
         const int qrow = i0 + 16 * qt + 4 * b16 + r;
         const bool vis = qrow < N && key < N && (!CAUSAL || key <= qrow);
-        const float p = vis ? exp2_hw(fmaf(s[qt][r], c, -lv[r])) : 0.f;
+        const float e = exp2_hw(fmaf(s[qt][r], c, -lv[r]));
+        const float p = MASKED ? (vis ? e : 0.f) : e;
         s[qt][r] = p;
         dp[qt][r] = p * (dp[qt][r] - dl[r]);
       }
-    }
-    // dV += P^T dO and dK += dS^T Q over two 32-row halves: the A operand of
-    // half u2 is rows 32 u2 + 4 b16 + (0..3) and 32 u2 + 16 + 4 b16 + (0..3).
-#pragma unroll
-    for (int u2 = 0; u2 < 2; ++u2) {
+    };
+    // dV += P^T dO and dK += dS^T Q over the 32-row half u2: the A operand is
+    // rows 32 u2 + 4 b16 + (0..3) and 32 u2 + 16 + 4 b16 + (0..3). The
+    // transposed B fragments are read one 16-column step ahead.
+    i16x4 tr[2][4];
+    auto read_tr = [&](int u2, int tt) {
+      const int ro = u2 * 32 * C::CPR * 16;
+      tr[tt & 1][0] = lds_read_tr(db + troff[tt] + ro);
+      tr[tt & 1][1] = lds_read_tr(db + troff[tt] + ro + 16 * C::CPR * 16);
+      tr[tt & 1][2] = lds_read_tr(qb + troff[tt] + ro);
+      tr[tt & 1][3] = lds_read_tr(qb + troff[tt] + ro + 16 * C::CPR * 16);
+      asm volatile("" : "+v"(tr[tt & 1][0]), "+v"(tr[tt & 1][1]), "+v"(tr[tt & 1][2]), "+v"(tr[tt & 1][3]));
+    };
+    auto dvdk = [&](int u2) {
       const bf16x8 pa = pack_bf16x8(s[2 * u2][0], s[2 * u2][1], s[2 * u2][2], s[2 * u2][3],
                                     s[2 * u2 + 1][0], s[2 * u2 + 1][1], s[2 * u2 + 1][2], s[2 * u2 + 1][3]);
       const bf16x8 sa = pack_bf16x8(dp[2 * u2][0], dp[2 * u2][1], dp[2 * u2][2], dp[2 * u2][3],
                                     dp[2 * u2 + 1][0], dp[2 * u2 + 1][1], dp[2 * u2 + 1][2], dp[2 * u2 + 1][3]);
-      const int ro = u2 * 32 * C::CPR * 16;
+      read_tr(u2, 0);
 #pragma unroll
       for (int tt = 0; tt < C::TT; ++tt) {
-        const i16x4 dlo = lds_read_tr(db + troff[tt] + ro);
-        const i16x4 dhi = lds_read_tr(db + troff[tt] + ro + 16 * C::CPR * 16);
-        dv[tt] = mfma16(pa, join_bf16x8(dlo, dhi), dv[tt]);
-        const i16x4 qlo = lds_read_tr(qb + troff[tt] + ro);
-        const i16x4 qhi = lds_read_tr(qb + troff[tt] + ro + 16 * C::CPR * 16);
-        dk[tt] = mfma16(sa, join_bf16x8(qlo, qhi), dk[tt]);
+        if (tt + 1 < C::TT) read_tr(u2, tt + 1);
+        dv[tt] = mfma16(pa, join_bf16x8(tr[tt & 1][0], tr[tt & 1][1]), dv[tt]);
+        dk[tt] = mfma16(sa, join_bf16x8(tr[tt & 1][2], tr[tt & 1][3]), dk[tt]);
       }
-    }
+    };
+    // The weights of groups 0 and 1 are computed while the products of groups
+    // 2 and 3 run, those of groups 2 and 3 while the dV/dK products of rows
+    // 0..31 run (each call's instructions are independent of the other's).
+    read_a(0);
+    read_a(1);
+    sdp(0);
+    read_a(2);
+    sdp(1);
+    read_a(3);
+    sdp(2);
+    pds(0);
+    pds(1);
+    sdp(3);
+    dvdk(0);
+    pds(2);
+    pds(3);
+    dvdk(1);
+  };
+  auto tile = [&](auto buf_c, int t) {
+    constexpr int buf = decltype(buf_c)::value;
+    wait_vmem_all();
+    __syncthreads();
+    if (t + 1 < n_t) issue(t + 1, buf ^ 1);
+    const int i0 = (u_begin + t % per_head) * kBwdTile;
+    if (j0 + kBwdKeyBlock > N || i0 + kBwdTile > N || (CAUSAL && i0 < j0 + kBwdKeyBlock))
+      tile_body(buf_c, IC<1>{}, i0);
+    else
+      tile_body(buf_c, IC<0>{}, i0);
+  };
+  int t = 0;
+  for (; t + 1 < n_t; t += 2) {
+    tile(IC<0>{}, t);
+    tile(IC<1>{}, t + 1);
   }
+  if (t < n_t) tile(IC<0>{}, t);
 
   // Epilogue: lane holds keys j0 + 16 wave + 4 b16 + r, column 16 tt + j16.
   const float sc = a.scale;
