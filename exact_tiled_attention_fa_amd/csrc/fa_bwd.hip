@@ -543,14 +543,14 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
       p1 = mfma32(v1, df[kk], p1);
     }
     // dS^T = P^T (dP^T - delta); lane holds keys kv0 + 32 jt + 8 (r / 4) + 4 g + r % 4.
+    // Key kv0 + 4 g + o (o a compile-time offset) is visible to row qi iff
+    // o <= lim: one compare per weight (rows past N get lim = -1).
+    const int lim = (qi < N ? min(N - 1, CAUSAL ? qi : N - 1) : -1) - kv0 - 4 * g;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int o = 8 * (r >> 2) + 4 * g + (r & 3);
-      const int key0 = kv0 + o, key1 = kv0 + o + 32;
-      const bool v0 = key0 < N && qi < N && (!CAUSAL || key0 <= qi);
-      const bool v1 = key1 < N && qi < N && (!CAUSAL || key1 <= qi);
-      const float pa = v0 ? exp2_hw(fmaf(s0[r], c, -lse2)) : 0.f;
-      const float pb = v1 ? exp2_hw(fmaf(s1[r], c, -lse2)) : 0.f;
+      const int o = 8 * (r >> 2) + (r & 3);
+      const float pa = o <= lim ? exp2_hw(fmaf(s0[r], c, -lse2)) : 0.f;
+      const float pb = o + 32 <= lim ? exp2_hw(fmaf(s1[r], c, -lse2)) : 0.f;
       s0[r] = pa * (p0[r] - dl);
       s1[r] = pb * (p1[r] - dl);
     }
