@@ -30,7 +30,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
                                            untimed settle, for profilers:
                                            fwd-1x1x8192, fwd-1x1x8192-causal,
                                            fwd-1x32x4096, fwd-1x32x4096-causal,
-                                           fwd-1x8x131072-causal, decode,
+                                           fwd-1x8x131072-causal, decode, decode-varlen,
                                            bwd-1x32x4096, bwd-1x32x4096-causal,
                                            fwd-fp8-1x32x4096, fwd-fp8-1x32x4096-causal)
 """
@@ -198,15 +198,21 @@ def run_only(name: str, reps: int) -> None:
         fn = fa.prepare_bwd(q, k, v, o, lse, g, dq, dk, dv, ws, causal=case.causal, scale=case.scale)
         work = 10.0 * case.N ** 2 * case.d * case.B * case.Hq / (2 if case.causal else 1)
         unit = "TFLOP/s"
-    elif name == "decode":
+    elif name in ("decode", "decode-varlen"):
         case = si.DECODE_GQA
         q, k, v = (up(x) for x in si.decode_inputs(case))
         ws = torch.empty(fa.decode_workspace_bytes(case.B, case.Hq, case.L, case.d, case.num_splits),
                          dtype=torch.uint8, device=dev)
         o = torch.empty_like(q)
         lse = torch.empty((case.B, case.Hq), dtype=torch.float32, device=dev)
-        fn = fa.prepare_decode(q, k, v, o, lse, ws, num_splits=case.num_splits, scale=case.scale)
-        work = 2.0 * case.B * case.Hkv * case.L * case.d * 2
+        if name == "decode":
+            fn = fa.prepare_decode(q, k, v, o, lse, ws, num_splits=case.num_splits, scale=case.scale)
+            work = 2.0 * case.B * case.Hkv * case.L * case.d * 2
+        else:  # the main run's lengths: uniform in 1..L, seeded
+            lens = np.random.default_rng(case.seed).integers(1, case.L + 1, size=case.B).astype(np.int32)
+            fn = fa.prepare_decode(q, k, v, o, lse, ws, num_splits=case.num_splits, scale=case.scale,
+                                   seq_lens=torch.from_numpy(lens).to(dev))
+            work = 2.0 * int(lens.astype(np.int64).sum()) * case.Hkv * case.d * 2
         unit = "GB/s"
     else:
         raise SystemExit(f"unknown workload {name}")
