@@ -11,6 +11,9 @@ import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
+# The race-check build of the same sources (every LDS phase closed by a full
+# wait and a barrier); only the tests load it, to compare with libfa.so.
+SYNC_LIB_PATH = os.path.join(_PKG, "libfa_sync.so")
 
 FA_OK = 0
 STATUS_NAMES = {
@@ -96,6 +99,14 @@ def _load():
 
 def lib():
     return _load()
+
+
+def open_library(path: str):
+    """Load another build of the same C ABI (e.g. SYNC_LIB_PATH) with its
+    argument types declared; the package's own calls keep using libfa.so."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run exact_tiled_attention_fa_amd/build.py")
+    return _declare(ctypes.CDLL(path))
 
 
 def check(status: int, where: str) -> None:

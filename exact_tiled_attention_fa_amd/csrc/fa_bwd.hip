@@ -407,11 +407,13 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     wait_vmem_all();
     __syncthreads();
     if (t + 1 < n_t) issue(t + 1, buf ^ 1);
+    sync_check_group();
     const int i0 = (u_begin + t % per_head) * kBwdTile;
     if (j0 + kBwdKeyBlock > N || i0 + kBwdTile > N || (CAUSAL && i0 < j0 + kBwdKeyBlock))
       tile_body(buf_c, IC<1>{}, i0);
     else
       tile_body(buf_c, IC<0>{}, i0);
+    sync_check_group();
   };
   int t = 0;
   for (; t + 1 < n_t; t += 2) {
@@ -525,6 +527,7 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
       load_tile_at<D, kSw2>(kg, (t + 1) * kBwdTile, N, koffs, k_lds[buf ^ 1], wave);
       load_tile_at<D, kSwRows>(vg, (t + 1) * kBwdTile, N, voffs, v_lds[buf ^ 1], wave);
     }
+    sync_check_group();
     const int kv0 = t * kBwdTile;
     const char* kb = reinterpret_cast<const char*>(k_lds[buf]);
     const char* vb = reinterpret_cast<const char*>(v_lds[buf]);
@@ -575,6 +578,7 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
           dq[dt] = mfma32(join_bf16x8(lo, hi), sb[jt][hh], dq[dt]);
         }
       }
+    sync_check_group();
   }
 
   // Epilogue: lane holds row qi, columns 32 dt + 8 rq + 4 g + (0..3).

@@ -276,6 +276,7 @@ void fa_decode_split_kernel(DecArgs a) {
     l_run = fmaf(l_run, alpha, rs);
     if (lane < GM) alpha_lds[wave][lane] = alpha;
     wave_sync_lds();
+    sync_check_wave();
 
     // ---- O = alpha O + P V on the vector ALUs
     float al[GM];
@@ -300,6 +301,7 @@ void fa_decode_split_kernel(DecArgs a) {
         for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pv[hh], vv[e], o[hh][e]);
     }
     wave_sync_lds();
+    sync_check_wave();
   }
 
   // ---- per-wave totals: l over the 4 lanes of a head; O over the lanes sharing columns

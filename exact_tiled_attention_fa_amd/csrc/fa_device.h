@@ -58,6 +58,37 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Race-check build (compiled with -DFA_SYNC_CHECK=1): every phase of a kernel
+// that hands data through LDS, or fills LDS with direct loads, is closed by a
+// wait for all of the wave's outstanding memory operations (s_waitcnt 0) and,
+// where the whole work-group runs the phase, a work-group barrier; the
+// forward kernels also issue every direct load at the start of its step. The
+// arithmetic and its order do not change, so the race-check library must
+// reproduce the normal one bit for bit: a difference means that some read
+// met data that was not yet, or no longer, there.
+#ifndef FA_SYNC_CHECK
+#define FA_SYNC_CHECK 0
+#endif
+constexpr bool kSyncCheck = FA_SYNC_CHECK != 0;
+
+// Wave-level form: allowed anywhere, also in code the waves of a work-group
+// run a different number of times.
+__device__ __forceinline__ void sync_check_wave() {
+  if constexpr (kSyncCheck) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Work-group form: only where every wave of the work-group passes the same
+// number of times (beside the kernels' own __syncthreads()).
+__device__ __forceinline__ void sync_check_group() {
+  if constexpr (kSyncCheck) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
 // 16-byte global load with the non-temporal hint: for data read exactly once
 // (a KV cache in decode), so it does not displace reusable lines in the caches.
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));

@@ -400,12 +400,14 @@ void fa_fwd_kernel(FwdArgs a) {
   // they are issued at the start.
   auto step = [&](auto kb_c, int t, bool with_pv, bool spread) {
     constexpr int KB = decltype(kb_c)::value;
+    spread = spread && !kSyncCheck;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (!spread) {
       if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds[KB ^ 1]);
       issue(vg, vdo, true, t, v_lds[KB]);
     }
+    sync_check_group();
     if (kStageQ && !with_pv) read_q();
     const uint16_t* kbase = kg + (size_t)(t + 1) * kFwdKeys * D;
     const uint32_t kl0 = lds_addr(k_lds[KB ^ 1]) + 1024u * (uint32_t)(wave * C::BPW);
@@ -415,11 +417,13 @@ void fa_fwd_kernel(FwdArgs a) {
     if (with_pv) finish_p(pp0, pp1);
     f32x16 s0, s1;
     scores(reinterpret_cast<const char*>(k_lds[KB]), s0, s1, with_pv, spread, kbase, kl0);
+    sync_check_group();
     // Keep the packing and summing beside the score products: without this
     // the compiler sinks them past the mask branch, next to their first use.
     if (with_pv) asm volatile("" : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(l_run));
     softmax_pv((t_begin + t) * kFwdKeys, s0, s1, reinterpret_cast<const char*>(v_lds[KB ^ 1]), with_pv, spread,
                vbase, vl0);
+    sync_check_group();
   };
   auto last = [&](auto kb_c) {
     constexpr int KB = decltype(kb_c)::value;
@@ -427,6 +431,7 @@ void fa_fwd_kernel(FwdArgs a) {
     __syncthreads();
     finish_p(pp0, pp1);
     pv(reinterpret_cast<const char*>(v_lds[KB ^ 1]), false, nullptr, 0u);
+    sync_check_group();
   };
 
   // ---- the sweep: step 0 has no product to overlap; the steps in between go
@@ -483,6 +488,7 @@ void fa_fwd_kernel(FwdArgs a) {
                       oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
     }
   wave_sync_lds();
+  sync_check_group();
   // Row order: lane l takes 16-byte chunk l % (D / 8) of row l / (D / 8) + RPI i,
   // to the output or (split) to the split's partial row.
   constexpr int CPR16 = D / 8;

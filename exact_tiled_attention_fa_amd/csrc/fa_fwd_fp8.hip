@@ -400,12 +400,14 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 
   auto step = [&](auto kb_c, int t, bool with_pv, bool spread) {
     constexpr int KB = decltype(kb_c)::value;
+    spread = spread && !kSyncCheck;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (!spread) {
       if (t + 1 < n_tiles) issue(kg, kdo, false, t + 1, k_lds(KB ^ 1));
       issue(vg, vdo, true, t, v_lds(KB));
     }
+    sync_check_group();
     if (kStageQ && !with_pv) read_q();
     const uint8_t* kbase = kg + (size_t)(t + 1) * kTile8;
     const uint32_t kl0 = lds_addr(k_lds(KB ^ 1)) + 1024u * (uint32_t)(wave * BPW);
@@ -415,8 +417,10 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     if (with_pv) finish_p(pp0, pp1);
     f32x16 s0, s1;
     scores(k_lds(KB), s0, s1, with_pv, spread, kbase, kl0);
+    sync_check_group();
     if (with_pv) asm volatile("" : "+v"(pf), "+v"(l_run));
     softmax_pv((t_begin + t) * kFwdKeys, s0, s1, v_lds(KB ^ 1), with_pv, spread, vbase, vl0);
+    sync_check_group();
   };
   auto last = [&](auto kb_c) {
     constexpr int KB = decltype(kb_c)::value;
@@ -424,6 +428,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
     __syncthreads();
     finish_p(pp0, pp1);
     pv(v_lds(KB ^ 1), false, nullptr, 0u);
+    sync_check_group();
   };
 
   step(IC<0>{}, 0, false, false);
@@ -481,6 +486,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
                       oacc[dt][4 * rq + 2] * inv, oacc[dt][4 * rq + 3] * inv);
     }
   wave_sync_lds();
+  sync_check_group();
   constexpr int C16 = kD8 / 8;  // 16-byte chunks per BF16 row
   constexpr int RPI = 64 / C16;
   const int c16 = lane % C16;

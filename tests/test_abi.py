@@ -37,6 +37,17 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_race_check_build_exports_the_same_abi():
+    """libfa_sync.so (the -DFA_SYNC_CHECK=1 build the GPU race check compares
+    with libfa.so) is built beside it and exports every declared symbol."""
+    from exact_tiled_attention_fa_amd import _lib
+    sync = _lib.open_library(_lib.SYNC_LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(sync, name), name
+    assert sync.fa_status_string(-9).decode().startswith("FA_ERR_SCRATCH")
+    assert fwd(sync, d=96) == -3  # host checks run before any device work here too
+
+
 def test_status_strings(lib):
     from exact_tiled_attention_fa_amd import _lib
     for code, name in _lib.STATUS_NAMES.items():
