@@ -319,10 +319,13 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     const char* db = reinterpret_cast<const char*>(do_lds[buf]);
 
     // S = Q K^T and dP = dO V^T for the group of 16 query rows qt, from
-    // fragments read one group ahead into alternating register sets (the
-    // empty asm statements keep each set's reads where they are written: left
-    // to itself the compiler read every fragment right before its product and
-    // waited for it, one read in flight).
+    // fragments read one group ahead into alternating register sets. A
+    // scheduling barrier after each set's reads keeps them where they are
+    // written (left to itself the compiler read every fragment right before
+    // its product, one read in flight); the wait for the data stays at its
+    // first use. (An empty asm statement naming the registers would also hold
+    // the reads in place, but as a use of the data it made the wave wait for
+    // every read right there.)
     f32x4 s[4], dp[4];
     bf16x8 fq[2][C::KK16], fd[2][C::KK16];
     auto read_a = [&](int qt) {
@@ -331,8 +334,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
         fq[qt & 1][kk] = *reinterpret_cast<const bf16x8*>(qb + aoff[kk] + qt * 16 * C::CPR * 16);
         fd[qt & 1][kk] = *reinterpret_cast<const bf16x8*>(db + aoff[kk] + qt * 16 * C::CPR * 16);
       }
-#pragma unroll
-      for (int kk = 0; kk < C::KK16; ++kk) asm volatile("" : "+v"(fq[qt & 1][kk]), "+v"(fd[qt & 1][kk]));
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto sdp = [&](int qt) {
       s[qt] = f32x4{};
@@ -361,7 +363,8 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     };
     // dV += P^T dO and dK += dS^T Q over the 32-row half u2: the A operand is
     // rows 32 u2 + 4 b16 + (0..3) and 32 u2 + 16 + 4 b16 + (0..3). The
-    // transposed B fragments are read one 16-column step ahead.
+    // transposed B fragments are read one 16-column step ahead (held in place
+    // as the A fragments are).
     i16x4 tr[2][4];
     auto read_tr = [&](int u2, int tt) {
       const int ro = u2 * 32 * C::CPR * 16;
@@ -369,7 +372,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
       tr[tt & 1][1] = lds_read_tr(db + troff[tt] + ro + 16 * C::CPR * 16);
       tr[tt & 1][2] = lds_read_tr(qb + troff[tt] + ro);
       tr[tt & 1][3] = lds_read_tr(qb + troff[tt] + ro + 16 * C::CPR * 16);
-      asm volatile("" : "+v"(tr[tt & 1][0]), "+v"(tr[tt & 1][1]), "+v"(tr[tt & 1][2]), "+v"(tr[tt & 1][3]));
+      __builtin_amdgcn_sched_barrier(0);
     };
     auto dvdk = [&](int u2) {
       const bf16x8 pa = pack_bf16x8(s[2 * u2][0], s[2 * u2][1], s[2 * u2][2], s[2 * u2][3],
