@@ -270,10 +270,10 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
 
   const TileOffsets<D, kSwQ> toff(wave, lane, N);
   const uint32_t st_off = 16u * (uint32_t)lane;
-  auto issue = [&](int t, int buf) {
-    const int hq = hk * G + t / per_head;
-    const int u = u_begin + t % per_head;
-    const size_t rb = (size_t)(b * a.Hq + hq);
+  // Tile t is query tile u of query head hk G + gq; (gq, u) step through the
+  // tiles in order, without a division per tile.
+  auto issue = [&](int gq, int u, int buf) {
+    const size_t rb = (size_t)(b * a.Hq + hk * G + gq);
     load_tile_at<D, kSwQ>(a.q + rb * N * D, u * kBwdTile, N, toff, q_lds[buf], wave);
     load_tile_at<D, kSwQ>(a.dout + rb * N * D, u * kBwdTile, N, toff, do_lds[buf], wave);
     if (wave == 0 && lane < 16) {  // lse2 and delta of the tile's 64 rows (256 B each)
@@ -303,7 +303,10 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   for (int tt = 0; tt < C::TT; ++tt) dk[tt] = dv[tt] = f32x4{};
 
   const float c = a.c;
-  issue(0, 0);  // n_t >= 1: the key block lies below N
+  issue(0, u_begin, 0);  // n_t >= 1: the key block lies below N
+  int u_cur = u_begin;                                     // query tile of tile t
+  int u_next = u_begin + 1 < n_u ? u_begin + 1 : u_begin;  // query tile and head of tile t + 1
+  int gq_next = u_begin + 1 < n_u ? 0 : 1;
   // One query tile; the buffer index is a compile-time constant (the loop
   // takes two tiles per trip), so every LDS address is a register plus an
   // immediate: with a run-time index each of the tile's 96 reads took an
@@ -409,9 +412,14 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     constexpr int buf = decltype(buf_c)::value;
     wait_vmem_all();
     __syncthreads();
-    if (t + 1 < n_t) issue(t + 1, buf ^ 1);
+    if (t + 1 < n_t) issue(gq_next, u_next, buf ^ 1);
     sync_check_group();
-    const int i0 = (u_begin + t % per_head) * kBwdTile;
+    const int i0 = u_cur * kBwdTile;
+    u_cur = u_next;
+    if (++u_next == n_u) {
+      u_next = u_begin;
+      ++gq_next;
+    }
     if (j0 + kBwdKeyBlock > N || i0 + kBwdTile > N || (CAUSAL && i0 < j0 + kBwdKeyBlock))
       tile_body(buf_c, IC<1>{}, i0);
     else
