@@ -62,9 +62,6 @@ __device__ __forceinline__ int sw2(int r) {
   if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
   return (((r >> 1) & 1) << 1) | (((r >> 2) & 1) << 2) | ((r >> 3) & 1);
 }
-// Swizzle of tiles read by rows only (as the forward's K tiles).
-template <int D>
-__device__ __forceinline__ int swr(int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); }
 
 // Swizzle of the dK/dV pass's Q and dO tiles, read by rows (16 rows at one
 // chunk) and transposed with rows 4 b + (lane / 4) % 4 for 16-lane block b.
@@ -89,11 +86,11 @@ __device__ __forceinline__ int swq(int r) {
   return (h << 1) | ((t >> 2) & 1);
 }
 
-// Swizzle kinds of a tile: rows only, sw2 (dQ's K tiles), swq (dK/dV's Q, dO).
-enum { kSwRows = 0, kSw2 = 1, kSwQ = 2 };
+// Swizzle kinds of a tile: sw2 (dQ's K and V tiles), swq (dK/dV's Q, dO).
+enum { kSw2 = 1, kSwQ = 2 };
 template <int D, int SW>
 __device__ __forceinline__ int swz(int r) {
-  return SW == kSwQ ? swq<D>(r) : (SW == kSw2 ? sw2<D>(r) : swr<D>(r));
+  return SW == kSwQ ? swq<D>(r) : sw2<D>(r);
 }
 
 // Direct loads of the 64-row tile starting at row row0 of a row-major
@@ -101,30 +98,14 @@ __device__ __forceinline__ int swz(int r) {
 // BPW w .. BPW w + BPW - 1; lane l writes physical chunk l % CPR of its row
 // with logical chunk (l % CPR) ^ sw. The base moves to the tile's first row in
 // 64-bit arithmetic, so each lane's 32-bit byte offset spans one tile (at most
-// 16 KiB) whatever the sequence length. Rows past `rows` read the last row
-// (finite data the caller masks).
-template <int D, int SW>
-__device__ __forceinline__ void load_tile(const uint16_t* src, int row0, int rows, uint4* dst, int wave, int lane) {
-  using C = BwdCfg<D>;
-  const int pc = lane % C::CPR;
-  const uint32_t l0 = lds_addr(dst) + 1024u * (uint32_t)(C::BPW * wave);
-  const uint16_t* base = src + (size_t)row0 * D;
-  const int last = rows - 1 - row0;  // >= 0: a tile starts below `rows`
-#pragma unroll
-  for (int x = 0; x < C::BPW; ++x) {
-    const int r = C::RPB * (C::BPW * wave + x) + lane / C::CPR;
-    const int sw = swz<D, SW>(r);
-    const int row = min(r, last);
-    dma16(base, 2u * (uint32_t)(row * D + 8 * (pc ^ sw)), l0 + 1024u * x);
-  }
-}
-
-// Per-lane byte offsets, within a full 64-row tile, of load_tile's direct
-// loads. Computed once per work-group and kept in registers for the sweep: a
-// load's offset register must not be overwritten while the load is in flight,
-// so offsets computed afresh for every tile made the compiler wait for the
-// next tile's loads before the current tile's first LDS reads (which reused
-// those registers), undoing the double buffering.
+// 16 KiB) whatever the sequence length.
+//
+// The per-lane byte offsets within a full tile are computed once per
+// work-group and kept in registers for the sweep: a load's offset register
+// must not be overwritten while the load is in flight, so offsets computed
+// afresh for every tile made the compiler wait for the next tile's loads
+// before the current tile's first LDS reads (which reused those registers),
+// undoing the double buffering.
 // The only ragged tile of a sweep is the last one, whose rows past the end
 // read row (rows - 1) % 64 of the tile (finite data the caller masks); its
 // clamped offsets are precomputed the same way.
@@ -483,10 +464,9 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const int kv_end = CAUSAL ? min(N, q0 + kBwdRowBlock) : N;
   const int n_tiles = (kv_end + kBwdTile - 1) / kBwdTile;
 
-  const TileOffsets<D, kSw2> koffs(wave, lane, N);
-  const TileOffsets<D, kSwRows> voffs(wave, lane, N);
+  const TileOffsets<D, kSw2> koffs(wave, lane, N);  // K and V tiles alike
   load_tile_at<D, kSw2>(kg, 0, N, koffs, k_lds[0], wave);
-  load_tile_at<D, kSwRows>(vg, 0, N, voffs, v_lds[0], wave);
+  load_tile_at<D, kSw2>(vg, 0, N, koffs, v_lds[0], wave);
 
   // Q^T and dO^T as B operands (lane = query row qi), lse2 and delta of qi.
   bf16x8 qf[C::KK32], df[C::KK32];
@@ -504,13 +484,13 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   const float lse2 = a.lse2[st];
   const float dl = a.delta[st];
 
-  // LDS offsets. K rows (sw2) and V rows (swr): row li, chunk 2 kk + g.
-  int koff[C::KK32], voff[C::KK32];
+  // LDS offsets of the row reads: row li, chunk 2 kk + g. The V tiles take the
+  // K tiles' swizzle (sw2, conflict-free for these reads too), so one set of
+  // offsets serves both; the 16 registers this saves hold the fragments read
+  // one k-step ahead.
+  int koff[C::KK32];
 #pragma unroll
-  for (int kk = 0; kk < C::KK32; ++kk) {
-    koff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ sw2<D>(li)));
-    voff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ swr<D>(li)));
-  }
+  for (int kk = 0; kk < C::KK32; ++kk) koff[kk] = 16 * (li * C::CPR + ((2 * kk + g) ^ sw2<D>(li)));
   // K^T transposed reads (as the forward's V^T): lane t16 names row
   // 4 g + t16 / 4 (+ 32 jt + 16 hh, + 8 for the upper 4 keys) and 4 columns at
   // 32 dt + 16 vch + 4 (t16 % 4). sw2 of those rows depends on the +8 only.
@@ -536,25 +516,34 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
     __syncthreads();
     if (t + 1 < n_tiles) {
       load_tile_at<D, kSw2>(kg, (t + 1) * kBwdTile, N, koffs, k_lds[buf ^ 1], wave);
-      load_tile_at<D, kSwRows>(vg, (t + 1) * kBwdTile, N, voffs, v_lds[buf ^ 1], wave);
+      load_tile_at<D, kSw2>(vg, (t + 1) * kBwdTile, N, koffs, v_lds[buf ^ 1], wave);
     }
     sync_check_group();
     const int kv0 = t * kBwdTile;
     const char* kb = reinterpret_cast<const char*>(k_lds[buf]);
     const char* vb = reinterpret_cast<const char*>(v_lds[buf]);
 
-    // S^T = K Q^T and dP^T = V dO^T for two 32-key halves.
+    // S^T = K Q^T and dP^T = V dO^T for two 32-key halves, the K and V
+    // fragments of k-step kk + 1 read while the products of step kk run
+    // (alternating register sets; a scheduling barrier keeps each step's reads
+    // in place, the waits stay at the first use).
     f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+    bf16x8 fk[2][2], fv[2][2];
+    auto read_kv = [&](int kk) {
+      fk[kk & 1][0] = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
+      fk[kk & 1][1] = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
+      fv[kk & 1][0] = *reinterpret_cast<const bf16x8*>(vb + koff[kk]);
+      fv[kk & 1][1] = *reinterpret_cast<const bf16x8*>(vb + koff[kk] + 32 * C::CPR * 16);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    read_kv(0);
 #pragma unroll
     for (int kk = 0; kk < C::KK32; ++kk) {
-      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
-      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kb + koff[kk] + 32 * C::CPR * 16);
-      const bf16x8 v0 = *reinterpret_cast<const bf16x8*>(vb + voff[kk]);
-      const bf16x8 v1 = *reinterpret_cast<const bf16x8*>(vb + voff[kk] + 32 * C::CPR * 16);
-      s0 = mfma32(k0, qf[kk], s0);
-      s1 = mfma32(k1, qf[kk], s1);
-      p0 = mfma32(v0, df[kk], p0);
-      p1 = mfma32(v1, df[kk], p1);
+      if (kk + 1 < C::KK32) read_kv(kk + 1);
+      s0 = mfma32(fk[kk & 1][0], qf[kk], s0);
+      s1 = mfma32(fk[kk & 1][1], qf[kk], s1);
+      p0 = mfma32(fv[kk & 1][0], df[kk], p0);
+      p1 = mfma32(fv[kk & 1][1], df[kk], p1);
     }
     // dS^T = P^T (dP^T - delta); lane holds keys kv0 + 32 jt + 8 (r / 4) + 4 g + r % 4.
     // Key kv0 + 4 g + o (o a compile-time offset) is visible to row qi iff
