@@ -510,7 +510,14 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   for (int dt = 0; dt < C::DT; ++dt) dq[dt] = f32x16{};
   const float c = a.c;
 
-  for (int t = 0; t < n_tiles; ++t) {
+  // One key tile. MASKED for the tiles that hold keys past N or (causal) keys
+  // above a row of the block: the tail of the sweep, from t_edge on (below,
+  // the loop splits there so that the other tiles take no compare per weight,
+  // a quarter of a tile's vector instructions; a branch inside the tile body
+  // instead made the d = 128 kernel spill). Rows past N need no mask: their
+  // dQ columns are never stored, and the products keep columns apart.
+  auto tile = [&](int t, auto mask_c) {
+    constexpr bool MASKED = decltype(mask_c)::value != 0;
     const int buf = t & 1;
     wait_vmem_all();
     __syncthreads();
@@ -552,8 +559,10 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int o = 8 * (r >> 2) + (r & 3);
-      const float pa = o <= lim ? exp2_hw(fmaf(s0[r], c, -lse2)) : 0.f;
-      const float pb = o + 32 <= lim ? exp2_hw(fmaf(s1[r], c, -lse2)) : 0.f;
+      const float ea = exp2_hw(fmaf(s0[r], c, -lse2));
+      const float eb = exp2_hw(fmaf(s1[r], c, -lse2));
+      const float pa = MASKED ? (o <= lim ? ea : 0.f) : ea;
+      const float pb = MASKED ? (o + 32 <= lim ? eb : 0.f) : eb;
       s0[r] = pa * (p0[r] - dl);
       s1[r] = pb * (p1[r] - dl);
     }
@@ -579,7 +588,13 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
         }
       }
     sync_check_group();
-  }
+  };
+  // Tiles below t_edge hold only keys below N and (causal) below the block's
+  // first row q0 (a multiple of the tile), so every key is visible to every row.
+  const int t_edge = CAUSAL ? min(q0, N) / kBwdTile : N / kBwdTile;
+  int t = 0;
+  for (; t < t_edge && t < n_tiles; ++t) tile(t, IC<0>{});
+  for (; t < n_tiles; ++t) tile(t, IC<1>{});
 
   // Epilogue: lane holds row qi, columns 32 dt + 8 rq + 4 g + (0..3).
   if (qi < N) {
