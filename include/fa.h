@@ -204,9 +204,10 @@ int fa_decode(const void* q, const void* k, const void* v, void* o, float* lse,
  *            so it cannot be validated on the host.
  *   Every other argument, the layouts and the workspace
  *   (fa_decode_workspace_bytes(B, Hq, L, d, num_splits)) are those of
- *   fa_decode. Each sequence's own len_b keys are cut into the S chunks that
- *   fa_decode would use for L (ceil(len_b / S) keys each), so the work of a
- *   sequence spreads over all of its work-groups.
+ *   fa_decode. Each sequence's own len_b keys are cut into chunks of
+ *   max(ceil(len_b / S), 128) keys (at most the S that fa_decode would use
+ *   for L), so the work of a sequence spreads over its work-groups; chunks
+ *   past len_b are empty and take no part in the merge.
  */
 int fa_decode_varlen(const void* q, const void* k, const void* v, void* o, float* lse, const int* seq_lens,
                      int B, int Hq, int Hkv, int L, int d, int num_splits, float scale,
