@@ -63,6 +63,14 @@ def test_bwd_causal_head_groups(B, Hq, Hkv, N):
     _run_small(B, Hq, Hkv, N, True, seed=1400 + N + Hq)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_multi_query(causal, d):
+    """16 query heads over one KV head: each key block's dK and dV sum over all 16 heads' tiles in
+    one sweep."""
+    _run_small(1, 16, 1, 200, causal, seed=1450 + d + int(causal), d=d)
+
+
 @pytest.mark.parametrize("scale", [0.0, -0.2, 0.3])
 def test_bwd_scale_edge_cases(scale):
     _run_small(1, 2, 1, 300, True, seed=800, scale=scale)

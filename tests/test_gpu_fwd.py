@@ -152,6 +152,14 @@ def test_gqa_mapping(Hq, Hkv):
     _run_case(si.FwdCase(f"gqa {Hq}/{Hkv}", 2, Hq, Hkv, 256, 64, True, seed=50 + Hq + Hkv))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_multi_query(causal, d):
+    """One KV head for 32 query heads, two sequences: every query head of a sequence reads the same
+    K and V."""
+    _run_case(si.FwdCase(f"mqa 32/1 d{d}", 2, 32, 1, 300, d, causal, seed=55 + d + int(causal)))
+
+
 def test_run_to_run_bitwise_determinism():
     import torch
     import exact_tiled_attention_fa_amd as fa

@@ -134,7 +134,7 @@ def test_fp8_key_split(causal):
     _run("split 1x1x2048", 1, 1, 1, 2048, causal, seed=3101)
 
 
-@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 1)])
+@pytest.mark.parametrize("Hq,Hkv", [(8, 2), (8, 1), (32, 1)])
 def test_fp8_gqa(Hq, Hkv):
     _run(f"gqa {Hq}/{Hkv}", 1, Hq, Hkv, 384, True, seed=3200 + Hq * 10 + Hkv)
 
