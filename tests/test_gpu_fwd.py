@@ -174,6 +174,36 @@ def test_run_to_run_bitwise_determinism():
     assert not torch.equal(o1.view(torch.int16), o2.view(torch.int16))
 
 
+def test_fwd_on_concurrent_streams():
+    """fa_fwd on the key-split path takes its partial buffer from the stream-ordered pool of the call's
+    stream. Two streams, each running several calls back to back on its own inputs (both masks) with no
+    synchronisation between them, must each get exactly fa_fwd_ws's results."""
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    cases = [si.FwdCase("streams a", 1, 1, 1, 8192, 128, False, seed=91),
+             si.FwdCase("streams b", 1, 2, 1, 6000, 128, True, seed=92)]
+    assert all(fa.fwd_workspace_bytes(c.B, c.Hq, c.N, c.d) > 0 for c in cases)  # both take the split path
+    inputs = [tuple(to_dev(x) for x in si.fwd_inputs(c)) for c in cases]
+    refs = []
+    for c, (q, k, v) in zip(cases, inputs):
+        o = torch.empty_like(q)
+        lse = torch.empty((c.B, c.Hq, c.N), dtype=torch.float32, device=q.device)
+        fa.prepare_fwd(q, k, v, o, lse, causal=c.causal)()
+        refs.append((o, lse))
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[], []]
+    for rep in range(4):
+        for i, (c, (q, k, v)) in enumerate(zip(cases, inputs)):
+            with torch.cuda.stream(streams[i]):
+                outs[i].append(fa.fwd(q, k, v, causal=c.causal))
+    torch.cuda.synchronize()
+    for i, (o_ref, l_ref) in enumerate(refs):
+        for o, lse in outs[i]:
+            assert torch.equal(o.view(torch.int16), o_ref.view(torch.int16)), f"{cases[i].name}: O differs"
+            assert torch.equal(lse, l_ref), f"{cases[i].name}: lse differs"
+
+
 def test_equal_keys_give_mean_of_values_at_full_size():
     """Property at the 8K size: identical keys make every weight 1/N (causal: 1/(i+1))."""
     import torch
