@@ -124,7 +124,9 @@ int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
  * that GPU's array: calls that may overlap on one GPU (different streams,
  * different host threads) race and must be ordered by the caller. Each call
  * writes every partial it reads, so the array keeps the last call's contents
- * and needs no clearing.
+ * and needs no clearing. A call records only kernel launches (no memset, no
+ * allocation), so it may be captured in a HIP graph once one call on that
+ * device (outside the capture) has looked up the array's address.
  */
 int fa_fwd_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
