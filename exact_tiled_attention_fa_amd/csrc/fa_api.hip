@@ -348,7 +348,7 @@ extern "C" int fa_bwd(const void* q, const void* k, const void* v, const void* o
   a.dk = static_cast<uint16_t*>(dk);
   a.dv = static_cast<uint16_t*>(dv);
   a.lse2 = static_cast<float*>(workspace);
-  a.delta = a.lse2 + (size_t)B * Hq * npad;
+  a.ndelta = a.lse2 + (size_t)B * Hq * npad;
   a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.N = N; a.Npad = (int)npad;
   a.c = scale * fa::kLog2eHost;
   a.scale = scale;

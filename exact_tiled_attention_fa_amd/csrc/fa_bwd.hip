@@ -12,8 +12,9 @@
 // stored.
 //
 // Three launches:
-//   * row pass: lse2 = lse log2(e) and delta = rowsum(dO O) per query row
-//     (the forward's O; sum_j P_ij dP_ij = sum_t dO_it O_it);
+//   * row pass: lse2 = lse log2(e) and -delta = -rowsum(dO O) per query row
+//     (the forward's O; sum_j P_ij dP_ij = sum_t dO_it O_it); the dP products
+//     start their accumulation from -delta, so they yield dP - delta at once;
 //   * dK/dV: one work-group of 4 waves per (batch, KV head, 64-key block);
 //     each wave owns 16 keys and keeps K^T and V^T of them in registers as
 //     v_mfma_f32_16x16x32_bf16 B operands. It sweeps 64-row tiles of Q and dO
@@ -168,8 +169,8 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 }  // namespace
 
 // ---------------------------------------------------------------- row pass
-// D / 8 lanes per row (8 columns each): delta = sum_t dO O in FP32, lse2 = lse
-// log2(e); rows N .. Npad - 1 of each head get zeros.
+// D / 8 lanes per row (8 columns each): -delta = -sum_t dO O in FP32, lse2 =
+// lse log2(e); rows N .. Npad - 1 of each head get zeros.
 template <int D>
 __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
   constexpr int LPR = D / 8;
@@ -191,7 +192,7 @@ __global__ __launch_bounds__(256) void fa_bwd_rows_kernel(BwdArgs a) {
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) s += shfl_xor(s, m);
   if (c16 == 0) {
-    a.delta[row] = s;
+    a.ndelta[row] = -s;
     a.lse2[row] = n < a.N ? a.lse[bh * a.N + n] * kLog2e : 0.f;
   }
 }
@@ -203,7 +204,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
   using C = BwdCfg<D>;
   __shared__ uint4 q_lds[2][C::TILE_CHUNKS];
   __shared__ uint4 do_lds[2][C::TILE_CHUNKS];
-  __shared__ float4 st_lds[2][2][kBwdTile / 4];  // [buffer][lse2 | delta][rows / 4]
+  __shared__ float4 st_lds[2][2][kBwdTile / 4];  // [buffer][lse2 | -delta][rows / 4]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -257,10 +258,10 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     const size_t rb = (size_t)(b * a.Hq + hk * G + gq);
     load_tile_at<D, kSwQ>(a.q + rb * N * D, u * kBwdTile, N, toff, q_lds[buf], wave);
     load_tile_at<D, kSwQ>(a.dout + rb * N * D, u * kBwdTile, N, toff, do_lds[buf], wave);
-    if (wave == 0 && lane < 16) {  // lse2 and delta of the tile's 64 rows (256 B each)
+    if (wave == 0 && lane < 16) {  // lse2 and -delta of the tile's 64 rows (256 B each)
       const size_t off = rb * a.Npad + (size_t)u * kBwdTile;
       dma16(a.lse2 + off, st_off, lds_addr(&st_lds[buf][0][0]));
-      dma16(a.delta + off, st_off, lds_addr(&st_lds[buf][1][0]));
+      dma16(a.ndelta + off, st_off, lds_addr(&st_lds[buf][1][0]));
     }
   };
 
@@ -320,9 +321,10 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
       }
       __builtin_amdgcn_sched_barrier(0);
     };
+    // dP starts from -delta of its rows, so the products leave dP - delta.
     auto sdp = [&](int qt) {
       s[qt] = f32x4{};
-      dp[qt] = f32x4{};
+      dp[qt] = __builtin_bit_cast(f32x4, st_lds[buf][1][4 * qt + b16]);
 #pragma unroll
       for (int kk = 0; kk < C::KK16; ++kk) {
         s[qt] = mfma16(fq[qt & 1][kk], kf[kk], s[qt]);
@@ -332,9 +334,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
     // P and dS of group qt: lane holds key `key`, query rows i0 + 16 qt + 4 b16 + r.
     auto pds = [&](int qt) {
       const float4 l4 = st_lds[buf][0][4 * qt + b16];
-      const float4 d4 = st_lds[buf][1][4 * qt + b16];
       const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-      const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int qrow = i0 + 16 * qt + 4 * b16 + r;
@@ -342,7 +342,7 @@ void fa_bwd_dkdv_kernel(BwdArgs a, int nwg) {
         const float e = exp2_hw(fmaf(s[qt][r], c, -lv[r]));
         const float p = MASKED ? (vis ? e : 0.f) : e;
         s[qt][r] = p;
-        dp[qt][r] = p * (dp[qt][r] - dl[r]);
+        dp[qt][r] = p * dp[qt][r];
       }
     };
     // dV += P^T dO and dK += dS^T Q over the 32-row half u2: the A operand is
@@ -468,7 +468,7 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   load_tile_at<D, kSw2>(kg, 0, N, koffs, k_lds[0], wave);
   load_tile_at<D, kSw2>(vg, 0, N, koffs, v_lds[0], wave);
 
-  // Q^T and dO^T as B operands (lane = query row qi), lse2 and delta of qi.
+  // Q^T and dO^T as B operands (lane = query row qi), lse2 and -delta of qi.
   bf16x8 qf[C::KK32], df[C::KK32];
   {
     const size_t r = q_base + (size_t)(qi < N ? qi : 0) * D;
@@ -482,7 +482,7 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
   }
   const size_t st = (size_t)(b * a.Hq + h) * a.Npad + (qi < N ? qi : 0);
   const float lse2 = a.lse2[st];
-  const float dl = a.delta[st];
+  const float ndl_v = a.ndelta[st];
 
   // LDS offsets of the row reads: row li, chunk 2 kk + g. The V tiles take the
   // K tiles' swizzle (sw2, conflict-free for these reads too), so one set of
@@ -534,7 +534,17 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
     // fragments of k-step kk + 1 read while the products of step kk run
     // (alternating register sets; a scheduling barrier keeps each step's reads
     // in place, the waits stay at the first use).
-    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = f32x16{}, p1 = f32x16{};
+    // Every register of dP^T holds row qi: the products start from a tile of
+    // -delta and leave dP^T - delta. At d = 128 the tile is rebuilt per key
+    // tile (held over the sweep, its 16 registers made the kernel spill).
+    f32x16 ndl;
+    {
+      float v = ndl_v;
+      if constexpr (D == 128) asm volatile("" : "+v"(v));
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ndl[r] = v;
+    }
+    f32x16 s0 = f32x16{}, s1 = f32x16{}, p0 = ndl, p1 = ndl;
     bf16x8 fk[2][2], fv[2][2];
     auto read_kv = [&](int kk) {
       fk[kk & 1][0] = *reinterpret_cast<const bf16x8*>(kb + koff[kk]);
@@ -563,8 +573,8 @@ void fa_bwd_dq_kernel(BwdArgs a, int nwg) {
       const float eb = exp2_hw(fmaf(s1[r], c, -lse2));
       const float pa = MASKED ? (o <= lim ? ea : 0.f) : ea;
       const float pb = MASKED ? (o + 32 <= lim ? eb : 0.f) : eb;
-      s0[r] = pa * (p0[r] - dl);
-      s1[r] = pb * (p1[r] - dl);
+      s0[r] = pa * p0[r];
+      s1[r] = pb * p1[r];
     }
     bf16x8 sb[2][2];
 #pragma unroll

@@ -28,6 +28,7 @@
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -140,12 +141,13 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // Four floats to four BF16 (nearest even), packed little-end first.
+// Built as a vector so that each pair becomes one v_cvt_pk_bf16_f32 (assembled
+// from 16-bit halves, the compiler converted one value per instruction and
+// shifted and merged the halves).
 __device__ __forceinline__ uint2 pack_bf16x4(float a0, float a1, float a2, float a3) {
-  __bf16 b0 = (__bf16)a0, b1 = (__bf16)a1, b2 = (__bf16)a2, b3 = (__bf16)a3;
-  uint2 r;
-  r.x = (uint32_t)__builtin_bit_cast(uint16_t, b0) | ((uint32_t)__builtin_bit_cast(uint16_t, b1) << 16);
-  r.y = (uint32_t)__builtin_bit_cast(uint16_t, b2) | ((uint32_t)__builtin_bit_cast(uint16_t, b3) << 16);
-  return r;
+  bf16x4 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  return __builtin_bit_cast(uint2, r);
 }
 
 // Log-sum-exp merge of one row's S key-split partials (BF16 normalised

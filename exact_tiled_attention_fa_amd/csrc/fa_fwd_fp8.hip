@@ -46,8 +46,10 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* lds_byte_ptr) {
 }
 
 // Four FP32 values -> four E4M3 bytes (nearest even), first value lowest.
-__device__ __forceinline__ int pack_fp8x4(float a, float b, float c, float d) {
-  int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+// Both halves of the word are written, so `prev` (the word this one replaces)
+// only names the register: no zeroing move per word.
+__device__ __forceinline__ int pack_fp8x4(int prev, float a, float b, float c, float d) {
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, prev, false);
   return __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);
 }
 
@@ -270,7 +272,7 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) oacc[dt] = f32x16{};
   f32x16 pp0, pp1;  // p of the previous tile (FP32)
-  i32x8 pf;         // its P^T operand (E4M3): dword 4 jt + q holds keys 32 jt + 8 q + 4 g + 0..3
+  i32x8 pf = {};    // its P^T operand (E4M3): dword 4 jt + q holds keys 32 jt + 8 q + 4 g + 0..3
 
   auto scores = [&](const char* kb, f32x16& s0, f32x16& s1, bool valu, bool dma, const uint8_t* kbase,
                     uint32_t kl0) {
@@ -314,8 +316,8 @@ void fa_fwd_fp8_kernel(FwdArgs a) {
   auto finish_p = [&](const f32x16& p0, const f32x16& p1) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      pf[q] = pack_fp8x4(p0[4 * q], p0[4 * q + 1], p0[4 * q + 2], p0[4 * q + 3]);
-      pf[4 + q] = pack_fp8x4(p1[4 * q], p1[4 * q + 1], p1[4 * q + 2], p1[4 * q + 3]);
+      pf[q] = pack_fp8x4(pf[q], p0[4 * q], p0[4 * q + 1], p0[4 * q + 2], p0[4 * q + 3]);
+      pf[4 + q] = pack_fp8x4(pf[4 + q], p1[4 * q], p1[4 * q + 1], p1[4 * q + 2], p1[4 * q + 3]);
     }
     float ra = p0[0] + p1[0];
     float rb = p0[1] + p1[1];

@@ -250,7 +250,7 @@ struct BwdArgs {
   uint16_t* dk;
   uint16_t* dv;
   float* lse2;   // [B * Hq, Npad]
-  float* delta;  // [B * Hq, Npad]
+  float* ndelta;  // [B * Hq, Npad]: -delta (the products start from it)
   int B, Hq, Hkv, N, Npad;
   float c;       // scale * log2(e)
   float scale;
