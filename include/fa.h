@@ -217,7 +217,7 @@ int fa_decode_varlen(const void* q, const void* k, const void* v, void* o, float
 
 /*
  * fa_bwd_workspace_bytes -- bytes of device workspace fa_bwd needs: two FP32
- * values per query row (lse in base 2 and delta = rowsum(dO O)), each head's
+ * values per query row (lse in base 2 and -delta, delta = rowsum(dO O)), each head's
  * rows padded to a multiple of 64. 0 for invalid sizes.
  */
 size_t fa_bwd_workspace_bytes(int B, int Hq, int N, int d);
