@@ -301,6 +301,9 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
     """Check the arguments once and return a callable that re-issues the same
     forward with the least host work: one C call (fa_fwd_ws) on the current
     stream, with a workspace allocated here once when the keys are split.
+    call(after_attention=ev) makes that call through fa_fwd_ws_timed, which
+    records the torch.cuda.Event `ev` right after the attention kernel (before
+    the key-split merge).
 
     The tensors must stay alive and unmoved while the callable is used.
     """
@@ -316,17 +319,26 @@ def prepare_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Te
         scale = 1.0 / math.sqrt(d)
     device = _one_device(("q", q), ("k", k), ("v", v), ("out", out), ("lse", lse))
     fn = _lib.lib().fa_fwd_ws
+    fn_timed = _lib.lib().fa_fwd_ws_timed
     with torch.cuda.device(device):
         need = fwd_workspace_bytes(B, Hq, N, d)
     ws = torch.empty(need, dtype=torch.uint8, device=device) if need else None
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), lse.data_ptr(),
             B, Hq, Hkv, N, d, 1 if causal else 0, float(scale), ws.data_ptr() if ws is not None else None, need)
 
-    def call():
+    def call(after_attention: torch.cuda.Event | None = None):
         with torch.cuda.device(device):
-            st = fn(*args, torch.cuda.current_stream(device).cuda_stream)
+            stream = torch.cuda.current_stream(device)
+            if after_attention is None:
+                st = fn(*args, stream.cuda_stream)
+                name = "fa_fwd_ws"
+            else:
+                if not after_attention.cuda_event:  # torch creates the HIP event at its first record
+                    after_attention.record(stream)
+                st = fn_timed(*args, stream.cuda_stream, after_attention.cuda_event)
+                name = "fa_fwd_ws_timed"
         if st:
-            _lib.check(st, "fa_fwd_ws")
+            _lib.check(st, name)
     call.workspace = ws  # keeps the buffer alive with the callable
     return call
 

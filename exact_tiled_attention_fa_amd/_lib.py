@@ -63,6 +63,8 @@ def _declare(lib):
     lib.fa_fwd_workspace_bytes.restype = ctypes.c_size_t
     lib.fa_fwd_ws.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp]
     lib.fa_fwd_ws.restype = ctypes.c_int
+    lib.fa_fwd_ws_timed.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp, sz, vp, vp]
+    lib.fa_fwd_ws_timed.restype = ctypes.c_int
     lib.fa_fwd_noalloc.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, i, i, f, vp]
     lib.fa_fwd_noalloc.restype = ctypes.c_int
     lib.fa_fwd_noalloc_max_scratch_bytes.argtypes = []

@@ -111,7 +111,7 @@ FwdPlan plan_fwd(int B, int Hq, int N, int d, bool causal, bool fp8) {
 
 int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const void* v, void* o, float* lse,
                        int B, int Hq, int Hkv, int N, int d, int causal, float scale, void* ws,
-                       hipStream_t s) {
+                       hipStream_t s, hipEvent_t after_attention = nullptr) {
   fa::FwdArgs a;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
@@ -132,8 +132,24 @@ int launch_fwd_planned(const FwdPlan& p, const void* q, const void* k, const voi
   a.lse_part = ws ? reinterpret_cast<float*>(a.o_part + (size_t)B * Hq * N * p.n_splits * d) : nullptr;
   a.v_scale = 1.f;
   hipError_t e = fa::launch_fwd(a, d, causal != 0, s);
+  if (e == hipSuccess && after_attention) e = hipEventRecord(after_attention, s);
   if (e == hipSuccess && p.n_splits > 1) e = fa::launch_fwd_combine(a, d, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_LAUNCH;
+}
+
+int fwd_ws_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int Hq, int Hkv, int N,
+                int d, int causal, float scale, void* workspace, size_t workspace_bytes, hipStream_t s,
+                hipEvent_t after_attention) {
+  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
+  if (st != FA_OK) return st;
+  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
+  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, false);
+  if (p.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+  }
+  return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
+                            p.ws_bytes > 0 ? workspace : nullptr, s, after_attention);
 }
 
 }  // namespace
@@ -153,16 +169,17 @@ extern "C" size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d) {
 extern "C" int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int Hq, int Hkv, int N, int d, int causal, float scale,
                          void* workspace, size_t workspace_bytes, fa_stream_t stream) {
-  int st = check_fwd_args(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale);
-  if (st != FA_OK) return st;
-  if ((st = check_fwd_sizes(B, Hq, N, d)) != FA_OK) return st;
-  const FwdPlan p = plan_fwd(B, Hq, N, d, causal != 0, false);
-  if (p.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < p.ws_bytes) return FA_ERR_WORKSPACE;
-    if (!aligned16(workspace)) return FA_ERR_ALIGN;
-  }
-  return launch_fwd_planned(p, q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale,
-                            p.ws_bytes > 0 ? workspace : nullptr, reinterpret_cast<hipStream_t>(stream));
+  return fwd_ws_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, workspace, workspace_bytes,
+                     reinterpret_cast<hipStream_t>(stream), nullptr);
+}
+
+extern "C" int fa_fwd_ws_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                               void* workspace, size_t workspace_bytes, fa_stream_t stream,
+                               fa_event_t after_attention) {
+  if (!after_attention) return FA_ERR_NULL;
+  return fwd_ws_impl(q, k, v, o, lse, B, Hq, Hkv, N, d, causal, scale, workspace, workspace_bytes,
+                     reinterpret_cast<hipStream_t>(stream), reinterpret_cast<hipEvent_t>(after_attention));
 }
 
 extern "C" int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,

@@ -47,9 +47,11 @@
 extern "C" {
 #endif
 
-/* Same object as hipStream_t, declared without the HIP headers. */
+/* Same objects as hipStream_t and hipEvent_t, declared without the HIP headers. */
 struct ihipStream_t;
 typedef struct ihipStream_t* fa_stream_t;
+struct ihipEvent_t;
+typedef struct ihipEvent_t* fa_event_t;
 
 typedef enum {
   FA_OK = 0,
@@ -108,6 +110,19 @@ size_t fa_fwd_workspace_bytes(int B, int Hq, int N, int d);
 int fa_fwd_ws(const void* q, const void* k, const void* v, void* o, float* lse,
               int B, int Hq, int Hkv, int N, int d, int causal, float scale,
               void* workspace, size_t workspace_bytes, fa_stream_t stream);
+
+/*
+ * fa_fwd_ws_timed -- fa_fwd_ws that also records `after_attention` (a HIP
+ * event created by the caller) on `stream` right after the attention kernel's
+ * launch and before the key-split merge (the end of the call when it has no
+ * merge), so that the caller can time the attention kernel alone with events.
+ * Same operation, arguments, results and errors as fa_fwd_ws; after_attention
+ * must not be NULL (FA_ERR_NULL), and a failed record returns FA_ERR_LAUNCH.
+ */
+int fa_fwd_ws_timed(const void* q, const void* k, const void* v, void* o, float* lse,
+                    int B, int Hq, int Hkv, int N, int d, int causal, float scale,
+                    void* workspace, size_t workspace_bytes, fa_stream_t stream,
+                    fa_event_t after_attention);
 
 /*
  * fa_fwd_noalloc -- fa_fwd for callers that cannot allocate device memory

@@ -29,7 +29,7 @@ def test_header_declares_the_abi():
     assert _declared_functions() == ["fa_bwd", "fa_bwd_workspace_bytes", "fa_decode", "fa_decode_varlen",
                                      "fa_decode_workspace_bytes", "fa_fwd", "fa_fwd_fp8", "fa_fwd_fp8_ws",
                                      "fa_fwd_noalloc", "fa_fwd_noalloc_max_scratch_bytes",
-                                     "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_status_string"]
+                                     "fa_fwd_workspace_bytes", "fa_fwd_ws", "fa_fwd_ws_timed", "fa_status_string"]
 
 
 def test_every_declared_symbol_is_exported(lib):
@@ -114,6 +114,18 @@ def fwd_ws(lib, q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causa
 ])
 def test_fwd_ws_rejects(lib, kw, status):
     assert fwd_ws(lib, **kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1), (dict(N=0), -2), (dict(d=80), -3), (dict(Hq=3, Hkv=2), -4),
+    (dict(v=BAD), -5), (dict(causal=-1), -8), (dict(scale=float("-inf")), -8),
+])
+def test_fwd_ws_timed_rejects(lib, kw, status):
+    """fa_fwd_ws_timed applies fa_fwd_ws's checks (before any HIP call) and refuses a NULL event."""
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, Hq=1, Hkv=1, N=128, d=128, causal=0, scale=0.125, ws=P, wsb=0)
+    a.update(kw)
+    assert lib.fa_fwd_ws_timed(*a.values(), None, P) == status
+    assert lib.fa_fwd_ws_timed(P, P, P, P, P, 1, 1, 1, 128, 128, 0, 0.125, P, 0, None, None) == -1
 
 
 def test_fwd_workspace_size_rules(lib):

@@ -44,11 +44,12 @@ def test_counters_reported_only_for_matching_sources(tmp_path, monkeypatch):
 def test_traffic_reported_only_for_matching_sources(tmp_path, monkeypatch):
     f = tmp_path / "c.txt"
     monkeypatch.setattr(bench, "COUNTERS_FILE", str(f))
-    assert bench.measured_traffic() is None
-    f.write_text(f"# x\nhbm_bytes_per_launch: 12345\nkernel_source_sha256_16: {bench.kernel_source_hash()}\n")
-    assert bench.measured_traffic() == 12345.0
-    f.write_text("hbm_bytes_per_launch: 12345\nkernel_source_sha256_16: deadbeefdeadbeef\n")
-    assert bench.measured_traffic() is None
+    assert bench.measured_traffic() == (None, None)
+    f.write_text(f"# x\nhbm_bytes_per_launch: 12345\ncall_hbm_bytes: 20000\n"
+                 f"kernel_source_sha256_16: {bench.kernel_source_hash()}\n")
+    assert bench.measured_traffic() == (12345.0, 20000.0)
+    f.write_text("hbm_bytes_per_launch: 12345\ncall_hbm_bytes: 20000\nkernel_source_sha256_16: deadbeefdeadbeef\n")
+    assert bench.measured_traffic() == (None, None)
 
 
 def test_committed_counter_summary_is_consistent():

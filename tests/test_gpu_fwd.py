@@ -204,6 +204,37 @@ def test_fwd_on_concurrent_streams():
             assert torch.equal(lse, l_ref), f"{cases[i].name}: lse differs"
 
 
+@pytest.mark.parametrize("shape", [(1, 1, 8192, 128, False), (1, 2, 6000, 128, True), (2, 32, 2048, 64, False)],
+                         ids=["split", "split-causal", "single"])
+def test_fwd_ws_timed_matches_fwd_ws(shape):
+    """fa_fwd_ws_timed (the bench's way to time the attention kernel alone) gives fa_fwd_ws's results bit
+    for bit, and records its event between the call's start and end: before the merge on the key-split
+    path, at the end of the single launch otherwise."""
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    B, H, N, d, causal = shape
+    case = si.FwdCase("timed", B, H, H, N, d, causal, seed=97)
+    print(f"[timed] B{B} H{H} N{N} d{d} causal={causal}", flush=True)
+    q, k, v = (to_dev(x) for x in si.fwd_inputs(case))
+    o1, o2 = torch.empty_like(q), torch.empty_like(q)
+    l1 = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    l2 = torch.empty_like(l1)
+    fa.prepare_fwd(q, k, v, o1, l1, causal=causal)()
+    run = fa.prepare_fwd(q, k, v, o2, l2, causal=causal)
+    start, mid, end = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o2.fill_(float("nan"))
+        start.record()
+        run(after_attention=mid)
+        end.record()
+        torch.cuda.synchronize()
+        assert torch.equal(o2.view(torch.int16), o1.view(torch.int16)), f"rep {rep}: O differs"
+        assert torch.equal(l2, l1), f"rep {rep}: lse differs"
+        t_mid, t_end = start.elapsed_time(mid), start.elapsed_time(end)
+        assert 0.0 < t_mid <= t_end, (t_mid, t_end)
+
+
 def test_equal_keys_give_mean_of_values_at_full_size():
     """Property at the 8K size: identical keys make every weight 1/N (causal: 1/(i+1))."""
     import torch
