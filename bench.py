@@ -54,7 +54,7 @@ PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 PEAK_FP8_TFLOPS = 5000.0    # MI355X dense FP8 MFMA
 # The analytic H100 figures of "FlashAttention HBM bytes, one head, 8K" ("A strong
 # answer"): a model of one 8K head at d = 128 on an H100 SXM, printed there for context.
-# They are the page's model, not measurements and not this build's target.
+# They are the page's model: not measurements, and not a target.
 PAGES_H100_MODEL = {
     "source": "FlashAttention HBM bytes, one head, 8K (A strong answer): analytic model, not measured",
     "h100_bf16_dense_tflops": 989.0,
