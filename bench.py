@@ -349,8 +349,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the forward shards by head "
-              "with no exchange; see the design notes). Run with --gpus 1.", file=sys.stderr, flush=True)
+        print("bench.py measures one GPU: the library has no multi-GPU path (the forward would shard by head "
+              "with no exchange between GPUs). Run with --gpus 1.", file=sys.stderr, flush=True)
         return 2
 
     import numpy as np
