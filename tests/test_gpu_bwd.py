@@ -4,7 +4,8 @@ The GPU runs its own forward (o, lse), then the backward from those and a
 seeded upstream gradient; the oracle differentiates the exact attention of the
 same BF16-valued inputs. Small cases are gated element-wise by a bound derived
 from the kernels' arithmetic (gpu_helpers.bwd_elem_bounds); the 32-head 4K
-workload is checked on eight heads' sampled rows and keys by the same bound.
+workload is checked on eight heads' sampled rows and keys by the same bound, and
+on every head by an identity of the exact gradients (the dV column sums).
 """
 import sys
 
@@ -110,3 +111,35 @@ def test_bwd_32_heads_4k_sampled(causal):
     for name, got, ref, bnd in (("dq", dq, rq, bq), ("dk", dk, rk, bk), ("dv", dv, rv, bv)):
         got = np.stack([got[:, h, rows[n]] for n, h in enumerate(heads)], axis=1)
         check_grad(name, got, ref, pick(bnd), f"1x32x4096 causal={causal}")
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,N,d,causal", [(1, 32, 32, 4096, 128, False), (1, 32, 32, 4096, 128, True),
+                                                 (1, 32, 8, 4096, 128, True), (2, 8, 2, 3000, 64, False)],
+                         ids=["32x4k", "32x4k-causal", "gqa-causal", "d64-ragged"])
+def test_bwd_dv_column_sums_every_head(B, Hq, Hkv, N, d, causal):
+    """Every head at full size, by an identity of the exact gradients: each row of P sums to 1 over its
+    visible keys, so the keys' dV = P^T dO add up to the query rows' dO, sum_j dV_j = sum_i dO_i (per KV
+    head and column, summed over the heads of its group). The kernel's P is rounded to BF16 before the
+    product (relative error <= 2^-8, so at most 2^-8 sum_i |dO_i| over all keys) and dV is stored in BF16
+    (at most 2^-8 |dV_j| each); 2^-12 sum_i |dO_i| more covers the FP32 recomputation of P and the FP32
+    sums. The bound is a worst case that grows with N, so this catches errors of whole heads or groups
+    (mapping, grouping, scale, normalisation) on every head; single tiles are the sampled test's job."""
+    import torch
+    import exact_tiled_attention_fa_amd as fa
+    what = f"B{B} Hq{Hq} Hkv{Hkv} N{N} d{d} causal={causal}"
+    print(f"[bwd] dV column sums {what}", flush=True)
+    qb, kb, vb, gb = _inputs(B, Hq, Hkv, N, seed=41, d=d)
+    q, k, v, g = to_dev(qb), to_dev(kb), to_dev(vb), to_dev(gb)
+    o, lse = fa.fwd(q, k, v, causal=causal)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, g, causal=causal)
+    torch.cuda.synchronize()
+    G = Hq // Hkv
+    dv64 = dv.double()
+    g64 = g.double().reshape(B, Hkv, G, N, d)
+    lhs = dv64.sum(dim=2)                                   # [B, Hkv, d]
+    rhs = g64.sum(dim=(2, 3))
+    bound = 2.0 ** -8 * dv64.abs().sum(dim=2) + (2.0 ** -8 + 2.0 ** -12) * g64.abs().sum(dim=(2, 3))
+    err = (lhs - rhs).abs()
+    ratio = float((err / bound).max())
+    print(f"    {what}: max |sum dV - sum dO| / bound = {ratio:.3f}", flush=True)
+    assert torch.isfinite(dv64).all() and ratio <= 1.0, f"{what}: dV column sums off by {ratio:.3f} x the bound"
